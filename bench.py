@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE dispatch + combine on one MI355X, virtual EP ranks.
+
+A step is one pass of the whole hot path over one batch: ep_get_layout ->
+ep_dispatch -> ep_combine, inputs resident in HBM.  The default workload is the
+prefill shape: 4096 tokens x hidden 7168 bf16, 256 experts in 8 groups, top-4
+groups then top-8 experts, 8 virtual ranks, expert_alignment 128.  Expert
+outputs are a separate seeded bf16 buffer (what an expert GEMM would have
+written), so combine does not read the rows dispatch just wrote.
+
+Metric: dispatch+combine algorithmic HBM bytes per step / step time (GB/s), and
+tokens/s.  Algorithmic bytes: dispatch 2NH + 2NKH (bf16) or 2NH + NKH +
+4NK(H/128) (e4m3), combine 2NKH + 2NH.  Layout time counts inside the step.
+
+Prints ONE JSON line.  Extra keys beside the required ones: tokens_per_s,
+hbm_frac, per-kernel times, the measured copy/write ceilings, the roofline of
+the dominant kernel and the CPU oracle baseline.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "dispatch+combine HBM GB/s and % of peak; tokens/s at 4096×7168 top-8"
+KERNEL_SRC = os.path.join(ROOT, "combine_ep_get_amd", "csrc", "ep_get.hip")
+
+
+def algorithmic_bytes(w):
+    N, H, K = w.N, w.H, w.K
+    if w.fp8:
+        disp = 2 * N * H + N * K * H + 4 * N * K * (H // 128)
+    else:
+        disp = 2 * N * H + 2 * N * K * H
+    comb = 2 * N * K * H + 2 * N * H
+    return disp, comb
+
+
+def source_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprof counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = dict(re.findall(r"^(\w+):\s*(\S+)", open(path).read(), flags=re.M))
+    if kv.get("source_sha256") != source_sha():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, eo_bits, budget_s):
+    """The oracle as it stands, single-threaded, on the same prefill batch."""
+    import oracle
+    cap = oracle.capacity(w.N, w.K, w.E, w.A)
+    disp_b, comb_b = algorithmic_bytes(w)
+    reps, t_total = 0, 0.0
+    while t_total < budget_s or reps == 0:
+        t0 = time.perf_counter()
+        lay = oracle.layout(inp["topk_idx"], w.E, w.R, w.A)
+        if w.fp8:
+            oracle.dispatch_fp8(inp["x"], lay["slot_of"], cap)
+        else:
+            oracle.dispatch_bf16(inp["x"], lay["slot_of"], cap)
+        oracle.recv_meta(lay["slot_of"], inp["topk_weights"], cap)
+        oracle.combine(eo_bits, lay["slot_of"], inp["topk_weights"])
+        t_total += time.perf_counter() - t0
+        reps += 1
+    step_s = t_total / reps
+    return {"value": round((disp_b + comb_b) / step_s / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} full steps (layout+dispatch+combine) of the {w.name} batch, "
+                      f"{w.N} tokens, single thread, {step_s * 1e3:.1f} ms/step",
+            "tokens_per_s": round(w.N / step_s, 1)}
+
+
+def ceilings(nbytes=1 << 30):
+    """Measured HBM copy and pure-write bandwidth (GB/s) on this GPU."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_ep_get_amd", "_lib", "libepceil.so"))
+    lib.epc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.epc_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for name, fn, moved in (("copy", lambda: lib.epc_copy(b.data_ptr(), a.data_ptr(), nbytes, st), 2),
+                            ("write", lambda: lib.epc_write(a.data_ptr(), nbytes, 7, st), 1)):
+        for _ in range(3):
+            assert fn() == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_gbs"] = round(moved * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="workload id 1..5 (default 3, prefill)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle baseline budget; 0 skips it")
+    ap.add_argument("--no-ceiling", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (virtual EP ranks inside one GPU's "
+              f"HBM); --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import combine_ep_get_amd as ep
+    from combine_ep_get_amd import workloads as wl
+
+    w = wl.CONFIGS[args.config]
+    print(f"[bench] {w.desc}", file=sys.stderr, flush=True)
+    inp = wl.make_inputs(w, args.seed)
+    cap = ep.recv_capacity(w.N, w.K, w.E, w.R, w.A)
+    eo_bits = wl.make_expert_out(w, cap, args.seed)
+    dev = torch.device("cuda")
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    wts = torch.from_numpy(inp["topk_weights"]).to(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    eo = torch.from_numpy(eo_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    lay = ep.alloc_layout(w.N, w.K, w.E, w.R, w.A, dev)
+    recv = ep.alloc_recv(lay, w.H, w.fp8, dev)
+    y = torch.empty((w.N, w.H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ep.get_layout(idx, w.E, w.R, w.A, out=lay)
+        if ev is not None:
+            ev[1].record()
+        ep.dispatch(x, wts, lay, w.fp8, out=recv)
+        if ev is not None:
+            ev[2].record()
+        ep.combine(eo, lay, wts, out=y)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    lay_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    dis_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    com_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    ev_step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
+
+    disp_b, comb_b = algorithmic_bytes(w)
+    total_b = disp_b + comb_b
+    gbs = total_b / step_s / 1e9
+    if dis_ms.mean() >= com_ms.mean():
+        dom, dom_b, dom_ms = "dispatch", disp_b, dis_ms.mean()
+        dom_kernel = "dispatch_fp8" if w.fp8 else "dispatch_bf16"
+    else:
+        dom, dom_b, dom_ms = "combine", comb_b, com_ms.mean()
+        dom_kernel = "combine"
+    achieved = dom_b / (dom_ms * 1e-3) / 1e9
+    traffic = read_traffic(dom_kernel, w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3" if w.fp8 else "bf16",
+        "data": "synthetic (seeded numpy; see DESIGN.md input recipe)",
+        "config": {"workload": f"{w.name}: {w.N} tokens x hidden {w.H}, {w.E} experts, "
+                               f"top-{w.K}, {w.R} virtual ranks, expert_alignment {w.A}, "
+                               f"{'e4m3' if w.fp8 else 'bf16'} dispatch, {w.routing} routing",
+                   "num_tokens": w.N, "hidden": w.H, "num_experts": w.E, "num_topk": w.K,
+                   "num_ranks": w.R, "expert_alignment": w.A, "seed": args.seed,
+                   "parallelism": "1 GPU, virtual EP ranks"},
+        "tokens_per_s": round(w.N / step_s, 1),
+        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "bytes_per_step": total_b,
+        "kernel_ms": {"layout": round(float(lay_ms.mean()), 4),
+                      "dispatch": round(float(dis_ms.mean()), 4),
+                      "combine": round(float(com_ms.mean()), 4),
+                      "step_events": round(float(ev_step_ms.mean()), 4),
+                      "step_events_p10": round(float(np.percentile(ev_step_ms, 10)), 4),
+                      "step_events_p90": round(float(np.percentile(ev_step_ms, 90)), 4)},
+        "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
+    }
+    if not args.no_ceiling:
+        c = ceilings()
+        result["ceiling"] = c
+        result["frac_of_copy_ceiling"] = round(gbs / c["copy_gbs"], 4)
+    if args.cpu_seconds > 0:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, inp, eo_bits, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

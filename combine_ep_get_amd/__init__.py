@@ -1,0 +1,246 @@
+"""Python binding of ``libepget.so`` (MoE expert-parallel layout / dispatch /
+combine on one MI355X, virtual EP ranks).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels.  Tensors are torch CUDA (HIP) tensors; calls are enqueued on
+``torch.cuda.current_stream()``.  When the library is missing, every call
+raises -- there is no fallback of any kind.
+
+    lay = get_layout(topk_idx, num_experts, num_ranks, expert_alignment)
+    recv_x, recv_scales, recv_src_idx, recv_w = dispatch(x, topk_weights, lay, use_fp8)
+    y = combine(expert_out, lay, topk_weights)
+
+The names follow DeepEP's (DeepEP book ch.1 "positioning and version
+boundaries", sec. 1.1 and 1.4): num_tokens_per_rank, num_tokens_per_expert,
+is_token_in_rank, expert_alignment, num_experts.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libepget.so")
+
+EP_OK = 0
+EP_LAYOUT_ERR_INDEX = 1
+
+_lib = None
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_topk", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("num_ranks", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
+                ("use_fp8", ctypes.c_int32)]
+
+
+class EPError(RuntimeError):
+    def __init__(self, fn, code):
+        msg = lib().ep_status_str(code).decode()
+        super().__init__(f"{fn}: {msg} (status {code})")
+        self.code = code
+
+
+EXPORTS = ("ep_recv_capacity", "ep_workspace_bytes", "ep_get_layout", "ep_dispatch",
+           "ep_combine", "ep_layout_error", "ep_status_str")
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, P = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(Problem)
+        L.ep_recv_capacity.restype = i64
+        L.ep_recv_capacity.argtypes = [P]
+        L.ep_workspace_bytes.restype = i64
+        L.ep_workspace_bytes.argtypes = [P]
+        L.ep_get_layout.restype = ctypes.c_int
+        L.ep_get_layout.argtypes = [P] + [vp] * 9
+        L.ep_dispatch.restype = ctypes.c_int
+        L.ep_dispatch.argtypes = [P] + [vp] * 9 + [i64, vp]
+        L.ep_combine.restype = ctypes.c_int
+        L.ep_combine.argtypes = [P, vp, vp, vp, vp, i64, vp]
+        L.ep_layout_error.restype = ctypes.c_int
+        L.ep_layout_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
+        L.ep_status_str.restype = ctypes.c_char_p
+        L.ep_status_str.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def problem(num_tokens, hidden, num_topk, num_experts, num_ranks, expert_alignment=1,
+            use_fp8=False):
+    return Problem(int(num_tokens), int(hidden), int(num_topk), int(num_experts),
+                   int(num_ranks), int(expert_alignment), int(bool(use_fp8)))
+
+
+def recv_capacity(num_tokens, num_topk, num_experts, num_ranks, expert_alignment=1):
+    p = problem(num_tokens, 8, num_topk, num_experts, num_ranks, expert_alignment)
+    v = lib().ep_recv_capacity(ctypes.byref(p))
+    if v < 0:
+        raise ValueError("invalid problem sizes")
+    return int(v)
+
+
+def workspace_bytes(num_tokens, num_topk, num_experts, num_ranks, expert_alignment=1):
+    p = problem(num_tokens, 8, num_topk, num_experts, num_ranks, expert_alignment)
+    v = lib().ep_workspace_bytes(ctypes.byref(p))
+    if v < 0:
+        raise ValueError("invalid problem sizes")
+    return int(v)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != EP_OK:
+        raise EPError(fn, rc)
+
+
+def _need(t, dtype, shape, name):
+    import torch
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
+            or t.device.type != "cuda":
+        raise ValueError(f"{name}: need contiguous {dtype} {tuple(shape)} on the GPU, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
+@dataclass
+class Layout:
+    """Output of get_layout; ``slot_of`` (with the caller's topk_weights) is the
+    handle that dispatch and combine consume."""
+    num_tokens: int
+    num_topk: int
+    num_experts: int
+    num_ranks: int
+    expert_alignment: int
+    capacity: int
+    num_tokens_per_rank: object    # [R, R] int32
+    num_tokens_per_expert: object  # [R, E] int32
+    is_token_in_rank: object       # [N, R] uint8
+    num_recv_per_expert: object    # [E] int32
+    expert_slot_offset: object     # [E + 1] int32
+    slot_of: object                # [N, K] int32
+    workspace: object              # uint8, ep_workspace_bytes
+
+    def problem(self, hidden=8, use_fp8=False):
+        return problem(self.num_tokens, hidden, self.num_topk, self.num_experts,
+                       self.num_ranks, self.expert_alignment, use_fp8)
+
+
+def alloc_layout(num_tokens, num_topk, num_experts, num_ranks, expert_alignment=1,
+                 device="cuda"):
+    """Allocate (but do not compute) the layout outputs and workspace."""
+    import torch
+    N, K, E, R, A = num_tokens, num_topk, num_experts, num_ranks, expert_alignment
+    cap = recv_capacity(N, K, E, R, A)
+    ws = workspace_bytes(N, K, E, R, A)
+    i32, u8 = torch.int32, torch.uint8
+    return Layout(N, K, E, R, A, cap,
+                  torch.empty((R, R), dtype=i32, device=device),
+                  torch.empty((R, E), dtype=i32, device=device),
+                  torch.empty((N, R), dtype=u8, device=device),
+                  torch.empty((E,), dtype=i32, device=device),
+                  torch.empty((E + 1,), dtype=i32, device=device),
+                  torch.empty((N, K), dtype=i32, device=device),
+                  torch.empty((max(ws, 256),), dtype=u8, device=device))
+
+
+def get_layout(topk_idx, num_experts, num_ranks, expert_alignment=1, out=None):
+    """Routing layout of ``topk_idx`` [N, K] int32 (see ep_get_layout)."""
+    import torch
+    N, K = topk_idx.shape
+    if out is None:
+        out = alloc_layout(N, K, num_experts, num_ranks, expert_alignment, topk_idx.device)
+    if (out.num_experts, out.num_ranks, out.expert_alignment) != \
+            (num_experts, num_ranks, expert_alignment):
+        raise ValueError("get_layout: `out` was allocated for another problem")
+    _need(topk_idx, torch.int32, (out.num_tokens, out.num_topk), "topk_idx")
+    p = out.problem()
+    rc = lib().ep_get_layout(ctypes.byref(p), _ptr(topk_idx), _ptr(out.num_tokens_per_rank),
+                             _ptr(out.num_tokens_per_expert), _ptr(out.is_token_in_rank),
+                             _ptr(out.num_recv_per_expert), _ptr(out.expert_slot_offset),
+                             _ptr(out.slot_of), _ptr(out.workspace), _stream())
+    _check("ep_get_layout", rc)
+    return out
+
+
+def alloc_recv(layout, hidden, use_fp8=False, device="cuda", capacity=None):
+    import torch
+    cap = layout.capacity if capacity is None else capacity
+    if use_fp8:
+        recv_x = torch.empty((cap, hidden), dtype=torch.float8_e4m3fn, device=device)
+        scales = torch.empty((cap, hidden // 128), dtype=torch.float32, device=device)
+    else:
+        recv_x = torch.empty((cap, hidden), dtype=torch.bfloat16, device=device)
+        scales = None
+    return (recv_x, scales, torch.empty((cap,), dtype=torch.int32, device=device),
+            torch.empty((cap,), dtype=torch.float32, device=device))
+
+
+def dispatch(x, topk_weights, layout, use_fp8=False, out=None, with_meta=True):
+    """Scatter ``x`` [N, H] bf16 into expert-contiguous receive slots.
+
+    Returns (recv_x, recv_scales, recv_src_idx, recv_topk_weights); recv_x is
+    bf16 or float8_e4m3fn [cap, H]; recv_scales is [cap, H/128] fp32 or None.
+    With ``with_meta=False`` the per-slot source/weight tags are skipped.
+    """
+    import torch
+    N, H = x.shape
+    _need(x, torch.bfloat16, (layout.num_tokens, H), "x")
+    if out is None:
+        out = alloc_recv(layout, H, use_fp8, x.device)
+    recv_x, scales, src, rw = out
+    cap = recv_x.shape[0]
+    _need(recv_x, torch.float8_e4m3fn if use_fp8 else torch.bfloat16, (cap, H), "recv_x")
+    if use_fp8:
+        _need(scales, torch.float32, (cap, H // 128), "recv_scales")
+    if with_meta:
+        _need(src, torch.int32, (cap,), "recv_src_idx")
+        _need(rw, torch.float32, (cap,), "recv_topk_weights")
+        _need(topk_weights, torch.float32, (layout.num_tokens, layout.num_topk), "topk_weights")
+    p = layout.problem(H, use_fp8)
+    rc = lib().ep_dispatch(ctypes.byref(p), _ptr(x), _ptr(topk_weights if with_meta else None),
+                           _ptr(layout.slot_of), _ptr(layout.expert_slot_offset),
+                           _ptr(layout.num_recv_per_expert), _ptr(recv_x),
+                           _ptr(scales if use_fp8 else None),
+                           _ptr(src if with_meta else None), _ptr(rw if with_meta else None),
+                           cap, _stream())
+    _check("ep_dispatch", rc)
+    return recv_x, (scales if use_fp8 else None), src, rw
+
+
+def combine(expert_out, layout, topk_weights, out=None):
+    """Weighted top-k reduction of ``expert_out`` [cap, H] bf16 into token order."""
+    import torch
+    cap, H = expert_out.shape
+    _need(expert_out, torch.bfloat16, (cap, H), "expert_out")
+    _need(topk_weights, torch.float32, (layout.num_tokens, layout.num_topk), "topk_weights")
+    if out is None:
+        out = torch.empty((layout.num_tokens, H), dtype=torch.bfloat16, device=expert_out.device)
+    _need(out, torch.bfloat16, (layout.num_tokens, H), "y")
+    p = layout.problem(H)
+    rc = lib().ep_combine(ctypes.byref(p), _ptr(expert_out), _ptr(layout.slot_of),
+                          _ptr(topk_weights), _ptr(out), cap, _stream())
+    _check("ep_combine", rc)
+    return out
+
+
+def layout_error(layout):
+    """Synchronous: error flags of the last get_layout into ``layout``."""
+    v = ctypes.c_int32(0)
+    _check("ep_layout_error", lib().ep_layout_error(_ptr(layout.workspace), ctypes.byref(v),
+                                                    _stream()))
+    return int(v.value)

@@ -1,0 +1,62 @@
+// ceiling.hip -- plain streaming kernels used only to measure what this GPU's
+// HBM delivers (copy and pure write), and as the known-size reference when
+// scaling rocprof FETCH_SIZE / WRITE_SIZE counters.  Not part of the EP path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+constexpr int kThreads = 256;
+constexpr int kPer = 4;   // 16-byte chunks per thread
+
+__global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict__ src,
+                                                        u32x4* __restrict__ dst, int64_t n16) {
+  const int64_t base = ((int64_t)blockIdx.x * kThreads * kPer) + threadIdx.x;
+  u32x4 v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int64_t j = base + (int64_t)i * kThreads;
+    if (j < n16) v[i] = __builtin_nontemporal_load(src + j);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int64_t j = base + (int64_t)i * kThreads;
+    if (j < n16) __builtin_nontemporal_store(v[i], dst + j);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void write_kernel(u32x4* __restrict__ dst, int64_t n16,
+                                                         uint32_t value) {
+  const int64_t base = ((int64_t)blockIdx.x * kThreads * kPer) + threadIdx.x;
+  const u32x4 v = {value, value, value, value};
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int64_t j = base + (int64_t)i * kThreads;
+    if (j < n16) __builtin_nontemporal_store(v, dst + j);
+  }
+}
+}  // namespace
+
+extern "C" {
+// Copy `bytes` (multiple of 16, 16-byte aligned pointers) from src to dst.
+int epc_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 || ((uintptr_t)dst | (uintptr_t)src) % 16) return 1;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = (n16 + kThreads * kPer - 1) / (kThreads * kPer);
+  if (blocks == 0) return 0;
+  copy_kernel<<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src,
+                                                                      (u32x4*)dst, n16);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+// Fill `bytes` (multiple of 16, 16-byte aligned) with a 32-bit pattern.
+int epc_write(void* dst, int64_t bytes, uint32_t value, void* stream) {
+  if (bytes < 0 || bytes % 16 || (uintptr_t)dst % 16) return 1;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = (n16 + kThreads * kPer - 1) / (kThreads * kPer);
+  if (blocks == 0) return 0;
+  write_kernel<<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((u32x4*)dst, n16, value);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+}

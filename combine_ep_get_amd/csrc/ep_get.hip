@@ -1,0 +1,833 @@
+// ep_get.hip -- MoE expert-parallel layout / dispatch / combine for one
+// MI355X (gfx950), virtual EP ranks as partitions of one GPU's HBM.
+//
+// The operations (see include/ep_get.h for the full contract):
+//   layout   : per-expert / per-rank histograms, is_token_in_rank, padded
+//              expert offsets and a stable slot for every (token, k) pair.
+//              DeepEP book ch.1 "positioning and version boundaries",
+//              sec. 1.4 names the layout tensors; lesson 14 "DeepSeek DeepEP
+//              core architecture", practice task, fixes the queue order.
+//   dispatch : bit copy (bf16) or fused per-128-channel E4M3 quantise + copy
+//              of each token row into its K slots.  DeepEP walkthrough
+//              (2kiu.com) sec. 2.1 and 2.3; FlashMLA/DeepEP/DeepGEMM in
+//              practice (nlpx) sec. 4.1 for the per-block scale.
+//   combine  : fp32 weighted gather-reduce of the K expert rows, bf16 store.
+//              Lesson 14, sec. 3 (top-k weighted sum) and practice task.
+//
+// Nothing here is a contraction, so there is no MFMA: every kernel is bound by
+// HBM bandwidth (dispatch, combine) or by latency (layout).  Design points:
+//   - one 64-lane wavefront per token row; 16-byte accesses so that one wave
+//     instruction moves 1 KiB of a row (fully coalesced 128-byte lines);
+//   - the row is read once into VGPRs and stored K times (dispatch), or the K
+//     rows are all put in flight before the fp32 accumulation (combine);
+//   - streaming data uses non-temporal loads/stores so that the 14 KiB rows do
+//     not evict the small metadata from L2 / the Infinity Cache;
+//   - no order-dependent atomics decide a slot: in-block ranks come from
+//     per-wavefront 64-bit LDS masks (atomic OR, commutative) plus popcount,
+//     so every output is deterministic run to run;
+//   - no device-wide memset and no host sync: every word of every output is
+//     written by some kernel on each call.
+//
+// Build: hipcc --offload-arch=gfx950 -O3 -ffp-contract=off (products and sums
+// in combine are rounded separately, matching the contract bit for bit).
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "ep_get.h"
+
+#ifndef EP_NT_LOAD
+#define EP_NT_LOAD 1
+#endif
+#ifndef EP_NT_STORE
+#define EP_NT_STORE 1
+#endif
+#ifndef EP_COMBINE_NV
+#define EP_COMBINE_NV 2
+#endif
+
+namespace {
+
+constexpr int kThreads = 256;             // 4 wavefronts per block
+constexpr int kWaves = kThreads / 64;
+constexpr int kScanThreads = 1024;
+constexpr int kFillPerThread = 8;         // padding-fill: slots per thread
+constexpr int kFillSlots = kThreads * kFillPerThread;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- memory ops
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
+#if EP_NT_LOAD
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
+#if EP_NT_STORE
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int lane_value(int v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ---------------------------------------------------------------- formats
+// bf16 halves of a 32-bit word -> float32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bf16 bits, round to nearest even (adding 0x7FFF plus the lowest
+// kept bit carries exactly when the dropped half is above 1/2, or equal to
+// 1/2 with an odd kept part).  NaN stays a quiet NaN with its sign.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// float32 -> OCP E4M3FN code, round to nearest even, saturating at +-448.
+//  |y| >= 448     : largest finite code 0x7E (also +-inf)
+//  |y| >= 2^-6    : normal; keep 3 mantissa bits with RNE on bit 20 of the
+//                   float32 pattern, then rebias the exponent 127 -> 7
+//  |y| <  2^-6    : subnormal; code = rint(|y| * 2^9) in 0..8 (8 is the
+//                   smallest normal, which is then the right answer)
+//  NaN            : 0x7F with the sign
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
+  uint32_t u = __float_as_uint(y);
+  uint32_t s = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x7F800000u) {
+    code = 0x7Fu;
+  } else if (a >= 0x43E00000u) {
+    code = 0x7Eu;
+  } else if (a >= 0x3C800000u) {
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  } else {
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return s | code;
+}
+
+// ---------------------------------------------------------------- layout
+// Work split shared by the host (workspace sizing) and the launches: blocks
+// never straddle a source rank, so the per-source sums are sums over whole
+// blocks.  Block b covers chunk (b % CB) of source (b / CB); a chunk is C
+// tokens (the last chunk of a source may be shorter).
+struct Plan {
+  int32_t C, CB, B;
+  int64_t o_err, o_cnt, o_pre, o_rank, o_berr, bytes;
+};
+
+__host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+// Phase 1: per-block expert histogram, is_token_in_rank rows and per-block
+// per-rank token counts.  LDS atomics only count (order does not matter).
+__global__ __launch_bounds__(kThreads) void layout_count_kernel(
+    const int32_t* __restrict__ topk_idx, uint8_t* __restrict__ in_rank,
+    int32_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_rank, int32_t* __restrict__ blk_err,
+    int K, int E, int R, int L, int T, int CB, int C) {
+  __shared__ int hist[EP_MAX_EXPERTS];
+  __shared__ int rcnt[EP_MAX_RANKS];
+  __shared__ uint8_t flags[64 * EP_MAX_RANKS];
+  __shared__ int err;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x, src = b / CB, c = b % CB;
+  const int t0 = src * T + c * C;
+  const int t1 = src * T + min((c + 1) * C, T);
+  for (int e = tid; e < E; e += kThreads) hist[e] = 0;
+  for (int r = tid; r < R; r += kThreads) rcnt[r] = 0;
+  if (tid == 0) err = 0;
+  for (int sub = t0; sub < t1; sub += 64) {
+    const int nt = min(64, t1 - sub);
+    for (int q = tid; q < nt * R; q += kThreads) flags[q] = 0;
+    __syncthreads();
+    const int32_t* idx = topk_idx + (int64_t)sub * K;
+    for (int q = tid; q < nt * K; q += kThreads) {
+      int e = idx[q];
+      if (e >= 0 && e < E) {
+        atomicAdd(&hist[e], 1);
+        flags[(q / K) * R + e / L] = 1;
+      } else if (e != -1) {
+        err = EP_LAYOUT_ERR_INDEX;
+      }
+    }
+    __syncthreads();
+    uint8_t* out = in_rank + (int64_t)sub * R;
+    for (int q = tid; q < nt * R; q += kThreads) {
+      uint8_t v = flags[q];
+      out[q] = v;
+      if (v) atomicAdd(&rcnt[q % R], 1);
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < E; e += kThreads) blk_cnt[(int64_t)b * E + e] = hist[e];
+  for (int r = tid; r < R; r += kThreads) blk_rank[(int64_t)b * R + r] = rcnt[r];
+  if (tid == 0) blk_err[b] = err;
+}
+
+// Phase 2 (one block): per-expert exclusive prefix over blocks, receive
+// counts, padded exclusive scan over experts, per-source matrices, error word.
+__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
+    const int32_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_pre,
+    const int32_t* __restrict__ blk_rank, const int32_t* __restrict__ blk_err,
+    int32_t* __restrict__ err_word, int32_t* __restrict__ num_tokens_per_rank,
+    int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_recv,
+    int32_t* __restrict__ off, int B, int CB, int E, int R, int A) {
+  __shared__ int part[kScanThreads];
+  __shared__ int wsum[kScanThreads / 64];
+  const int tid = threadIdx.x;
+  const int S = kScanThreads / E;  // block slices per expert (E <= 1024)
+  const int e = tid % E, sl = tid / E;
+  const bool act = sl < S;
+  const int b0 = (int)((int64_t)B * sl / S), b1 = (int)((int64_t)B * (sl + 1) / S);
+  int sum = 0;
+  if (act)
+    for (int b = b0; b < b1; b++) sum += blk_cnt[(int64_t)b * E + e];
+  if (act) part[sl * E + e] = sum;
+  __syncthreads();
+  int tot = 0;
+  if (act) {
+    int pre = 0;
+    for (int s2 = 0; s2 < S; s2++) {
+      int v = part[s2 * E + e];
+      if (s2 < sl) pre += v;
+      tot += v;
+    }
+    for (int b = b0; b < b1; b++) {
+      int v = blk_cnt[(int64_t)b * E + e];
+      blk_pre[(int64_t)b * E + e] = pre;
+      pre += v;
+    }
+    if (sl == 0) num_recv[e] = tot;
+  }
+  // padded sizes: thread tid < E is (expert tid, slice 0) and holds its total
+  int x = (tid < E) ? (tot + A - 1) / A * A : 0;
+  const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  if (tid < 64) {
+    int v = (tid < kScanThreads / 64) ? wsum[tid] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int y = __shfl_up(v, d);
+      if (tid >= d) v += y;
+    }
+    if (tid < kScanThreads / 64) wsum[tid] = v;
+  }
+  __syncthreads();
+  if (w > 0) x += wsum[w - 1];
+  if (tid < E) off[tid + 1] = x;
+  if (tid == 0) off[0] = 0;
+  for (int q = tid; q < R * E; q += kScanThreads) {
+    const int s = q / E, ex = q % E;
+    int v = 0;
+    for (int b = s * CB; b < (s + 1) * CB; b++) v += blk_cnt[(int64_t)b * E + ex];
+    num_tokens_per_expert[q] = v;
+  }
+  for (int q = tid; q < R * R; q += kScanThreads) {
+    const int s = q / R, r = q % R;
+    int v = 0;
+    for (int b = s * CB; b < (s + 1) * CB; b++) v += blk_rank[(int64_t)b * R + r];
+    num_tokens_per_rank[q] = v;
+  }
+  int ev = 0;
+  for (int b = tid; b < B; b += kScanThreads) ev |= blk_err[b];
+  ev = __syncthreads_or(ev);
+  if (tid == 0) *err_word = ev ? EP_LAYOUT_ERR_INDEX : 0;
+}
+
+// Phase 3: stable slot of every pair.  Pairs are taken in (token, k) order,
+// 256 per round; within a wavefront each lane ORs its bit into the 64-bit LDS
+// mask of its expert, so the rank among equal experts is the popcount of the
+// lower lanes' bits, plus the counts of lower wavefronts, plus everything the
+// block and the earlier blocks of the same expert already placed.
+__global__ __launch_bounds__(kThreads) void layout_assign_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_pre,
+    const int32_t* __restrict__ off, int32_t* __restrict__ slot_of, int K, int E, int T,
+    int CB, int C) {
+  __shared__ int base[EP_MAX_EXPERTS];
+  __shared__ unsigned long long masks[kWaves][EP_MAX_EXPERTS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = blockIdx.x, src = b / CB, c = b % CB;
+  const int t0 = src * T + c * C;
+  const int t1 = src * T + min((c + 1) * C, T);
+  const int64_t p0 = (int64_t)t0 * K;
+  const int np = (t1 - t0) * K;
+  for (int e = tid; e < E; e += kThreads) {
+    base[e] = off[e] + blk_pre[(int64_t)b * E + e];
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ww++) masks[ww][e] = 0ull;
+  }
+  __syncthreads();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int r0 = 0; r0 < np; r0 += kThreads) {
+    const int p = r0 + tid;
+    int e = -1;
+    if (p < np) e = topk_idx[p0 + p];
+    const bool ok = (e >= 0 && e < E);
+    if (ok) atomicOr(&masks[w][e], 1ull << lane);
+    __syncthreads();
+    int slot = -1;
+    unsigned long long m = 0;
+    if (ok) {
+      m = masks[w][e];
+      int pre = 0;
+      for (int w2 = 0; w2 < w; w2++) pre += __popcll(masks[w2][e]);
+      slot = base[e] + pre + __popcll(m & below);
+    }
+    __syncthreads();
+    if (ok && (m & below) == 0ull) {  // lowest lane of this expert in this wave
+      atomicAdd(&base[e], __popcll(m));
+      masks[w][e] = 0ull;
+    }
+    __syncthreads();
+    if (p < np) slot_of[p0 + p] = slot;
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+// Padding / unused slots of [0, cap): source -1, weight 0.  A slot s below
+// off[E] belongs to the expert e with off[e] <= s < off[e+1] (binary search
+// over the offsets staged in LDS) and is padding iff s - off[e] >= count[e].
+__device__ __forceinline__ void fill_padding(int fb, const int32_t* __restrict__ off,
+                                             const int32_t* __restrict__ recv_cnt, int E,
+                                             int64_t cap, int32_t* __restrict__ recv_src,
+                                             float* __restrict__ recv_w, int* s_off, int* s_cnt) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += kThreads) {
+    s_off[e] = off[e];
+    if (e < E) s_cnt[e] = recv_cnt[e];
+  }
+  __syncthreads();
+  const int used = s_off[E];
+#pragma unroll
+  for (int j = 0; j < kFillPerThread; j++) {
+    const int64_t s = (int64_t)fb * kFillSlots + (int64_t)j * kThreads + tid;
+    if (s >= cap) break;
+    bool pad = true;
+    if (s < used) {
+      int lo = 0, hi = E;  // off[lo] <= s < off[hi]
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= s) lo = mid; else hi = mid;
+      }
+      pad = (s - s_off[lo]) >= s_cnt[lo];
+    }
+    if (pad) {
+      if (recv_src) recv_src[s] = -1;
+      if (recv_w) recv_w[s] = 0.0f;
+    }
+  }
+}
+
+// Slot of pair (t, lane) for lanes < K, -1 elsewhere or when out of range.
+__device__ __forceinline__ int load_slot(const int32_t* __restrict__ slot_of, int t, int K,
+                                         int lane, int64_t cap) {
+  int s = -1;
+  if (lane < K) {
+    s = slot_of[(int64_t)t * K + lane];
+    if (s < 0 || (int64_t)s >= cap) s = -1;
+  }
+  return s;
+}
+
+__device__ __forceinline__ void write_meta(int t, int K, int lane, int myslot,
+                                           const float* __restrict__ w,
+                                           int32_t* __restrict__ recv_src,
+                                           float* __restrict__ recv_w) {
+  if (lane < K && myslot >= 0) {
+    if (recv_src) recv_src[myslot] = t;
+    if (recv_w) recv_w[myslot] = w[(int64_t)t * K + lane];
+  }
+}
+
+// bf16 rows: one wavefront per token; NV 16-byte chunks per lane per pass.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
+    u32x4* __restrict__ recv_x, int32_t* __restrict__ recv_src, float* __restrict__ recv_w,
+    int N, int K, int E, int H8, int64_t cap, int tok_blocks) {
+  __shared__ int s_off[EP_MAX_EXPERTS + 1];
+  __shared__ int s_cnt[EP_MAX_EXPERTS];
+  if ((int)blockIdx.x >= tok_blocks) {
+    fill_padding(blockIdx.x - tok_blocks, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
+    return;
+  }
+  const int t = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  if (t >= N) return;
+  const int lane = threadIdx.x & 63;
+  const int myslot = load_slot(slot_of, t, K, lane, cap);
+  const u32x4* row = x + (int64_t)t * H8;
+  for (int base = 0; base < H8; base += 64 * NV) {
+    u32x4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int c = base + i * 64 + lane;
+      if (c < H8) v[i] = ld16(row + c);
+    }
+    for (int k = 0; k < K; k++) {
+      const int s = lane_value(myslot, k);
+      if (s < 0) continue;
+      u32x4* dst = recv_x + (int64_t)s * H8;
+#pragma unroll
+      for (int i = 0; i < NV; i++) {
+        const int c = base + i * 64 + lane;
+        if (c < H8) st16(dst + c, v[i]);
+      }
+    }
+  }
+  write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+}
+
+// e4m3 rows: one wavefront per token.  A lane owns 16 consecutive channels
+// (two 16-byte bf16 loads, one 16-byte code store); 8 lanes form a
+// 128-channel group whose amax is reduced with xor-shuffles.  NI iterations
+// of 1024 channels per pass.  After iteration i, lanes 8i..8i+7 pick up the
+// scales of groups 8i..8i+7 so that one store per slot writes 64 scales.
+template <int NI>
+__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
+    u32x4* __restrict__ recv_q, float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
+    float* __restrict__ recv_w, int N, int K, int E, int H, int64_t cap, int tok_blocks) {
+  __shared__ int s_off[EP_MAX_EXPERTS + 1];
+  __shared__ int s_cnt[EP_MAX_EXPERTS];
+  if ((int)blockIdx.x >= tok_blocks) {
+    fill_padding(blockIdx.x - tok_blocks, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
+    return;
+  }
+  const int t = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  if (t >= N) return;
+  const int lane = threadIdx.x & 63;
+  const int myslot = load_slot(slot_of, t, K, lane, cap);
+  const int H8 = H >> 3, H16 = H >> 4, G = H >> 7;
+  const u32x4* row = x + (int64_t)t * H8;
+  for (int pbase = 0; pbase < H; pbase += NI * 1024) {
+    u32x4 v[NI][2];
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int ch = pbase + i * 1024 + lane * 16;
+      if (ch < H) {
+        v[i][0] = ld16(row + (ch >> 3));
+        v[i][1] = ld16(row + (ch >> 3) + 1);
+      }
+    }
+    float my_scale = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const int ch = pbase + i * 1024 + lane * 16;
+      float f[16];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        f[2 * j] = bf16_lo(v[i][0][j]);
+        f[2 * j + 1] = bf16_hi(v[i][0][j]);
+        f[8 + 2 * j] = bf16_lo(v[i][1][j]);
+        f[8 + 2 * j + 1] = bf16_hi(v[i][1][j]);
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(f[j]));
+      am = fmaxf(am, __shfl_xor(am, 1));
+      am = fmaxf(am, __shfl_xor(am, 2));
+      am = fmaxf(am, __shfl_xor(am, 4));
+      const bool zero = (am == 0.0f);
+      const float scale = zero ? 1.0f : am / 448.0f;
+      const float inv = 448.0f / am;
+      u32x4 q;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const float fv = f[4 * j + b];
+          const uint32_t code = zero ? ((__float_as_uint(fv) >> 24) & 0x80u)
+                                     : e4m3_rne_sat(fv * inv);
+          word |= code << (8 * b);
+        }
+        q[j] = word;
+      }
+      const float sv = __shfl(scale, 8 * (lane & 7));
+      if ((lane >> 3) == i) my_scale = sv;
+      if (ch < H) {
+        for (int k = 0; k < K; k++) {
+          const int s = lane_value(myslot, k);
+          if (s < 0) continue;
+          st16(recv_q + (int64_t)s * H16 + (ch >> 4), q);
+        }
+      }
+    }
+    const int g = (pbase >> 7) + lane;
+    if (lane < NI * 8 && g < G) {
+      for (int k = 0; k < K; k++) {
+        const int s = lane_value(myslot, k);
+        if (s < 0) continue;
+        recv_scales[(int64_t)s * G + g] = my_scale;
+      }
+    }
+  }
+  write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+}
+
+// ---------------------------------------------------------------- combine
+// One wavefront per token.  For each pass of NV 16-byte chunks per lane, the
+// rows of up to 8 pairs are loaded first (all in flight), then accumulated in
+// ascending k: acc = acc + w_k * row_k (separately rounded mul and add).
+template <int NV>
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const u32x4* __restrict__ eo, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ w, u32x4* __restrict__ y, int N, int K, int H8, int64_t cap) {
+  const int t = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  if (t >= N) return;
+  const int lane = threadIdx.x & 63;
+  const int myslot = load_slot(slot_of, t, K, lane, cap);
+  const float myw = (lane < K) ? w[(int64_t)t * K + lane] : 0.0f;
+  u32x4* yrow = y + (int64_t)t * H8;
+  for (int base = 0; base < H8; base += 64 * NV) {
+    float acc[NV][8];
+#pragma unroll
+    for (int i = 0; i < NV; i++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) acc[i][j] = 0.0f;
+    for (int kg = 0; kg < K; kg += 8) {
+      u32x4 v[8][NV];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int k = kg + j;
+        const int s = (k < K) ? lane_value(myslot, k) : -1;
+        if (s >= 0) {
+          const u32x4* r = eo + (int64_t)s * H8;
+#pragma unroll
+          for (int i = 0; i < NV; i++) {
+            const int c = base + i * 64 + lane;
+            if (c < H8) v[j][i] = ld16(r + c);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int k = kg + j;
+        const int s = (k < K) ? lane_value(myslot, k) : -1;
+        if (s < 0) continue;
+        const float wk = lane_value(myw, k);
+#pragma unroll
+        for (int i = 0; i < NV; i++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            acc[i][2 * q] = acc[i][2 * q] + wk * bf16_lo(v[j][i][q]);
+            acc[i][2 * q + 1] = acc[i][2 * q + 1] + wk * bf16_hi(v[j][i][q]);
+          }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int c = base + i * 64 + lane;
+      if (c < H8) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          o[q] = bf16_rne(acc[i][2 * q]) | (bf16_rne(acc[i][2 * q + 1]) << 16);
+        st16(yrow + c, o);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+bool log_on() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("EP_GET_LOG");
+    v = (e && *e && *e != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+#define EP_LOG(...)                          \
+  do {                                       \
+    if (log_on()) {                          \
+      fprintf(stderr, "[ep_get] " __VA_ARGS__); \
+      fputc('\n', stderr);                   \
+    }                                        \
+  } while (0)
+
+int check_device() {
+  static std::atomic<int> cache[64];  // 0 unknown, 1 gfx950, 2 other
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
+  int c = (dev >= 0 && dev < 64) ? cache[dev].load() : 0;
+  if (c == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return EP_ERR_HIP;
+    c = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    if (dev >= 0 && dev < 64) cache[dev].store(c);
+  }
+  return c == 1 ? EP_OK : EP_ERR_UNSUPPORTED;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    EP_LOG("%s: %s", what, hipGetErrorString(e));
+    return EP_ERR_HIP;
+  }
+  return EP_OK;
+}
+
+int64_t bound_of(const ep_problem_t* p) {
+  return (int64_t)p->num_tokens * p->num_topk + (int64_t)p->num_experts * (p->expert_alignment - 1);
+}
+
+int validate_layout(const ep_problem_t* p) {
+  if (!p) return EP_ERR_INVALID_ARG;
+  const int N = p->num_tokens, K = p->num_topk, E = p->num_experts, R = p->num_ranks,
+            A = p->expert_alignment;
+  if (N < 0 || K < 1 || K > EP_MAX_TOPK || E < 1 || E > EP_MAX_EXPERTS || R < 1 ||
+      R > EP_MAX_RANKS || R > E || A < 1)
+    return EP_ERR_INVALID_ARG;
+  if (E % R != 0 || N % R != 0) return EP_ERR_INVALID_ARG;
+  if (bound_of(p) > INT32_MAX) return EP_ERR_INVALID_ARG;
+  return EP_OK;
+}
+
+int validate_payload(const ep_problem_t* p) {
+  int rc = validate_layout(p);
+  if (rc != EP_OK) return rc;
+  const int H = p->hidden;
+  if (H <= 0 || H % 8 != 0) return EP_ERR_INVALID_ARG;
+  if (p->use_fp8 != 0 && p->use_fp8 != 1) return EP_ERR_INVALID_ARG;
+  if (p->use_fp8 && H % 128 != 0) return EP_ERR_INVALID_ARG;
+  return EP_OK;
+}
+
+Plan make_plan(const ep_problem_t* p) {
+  Plan pl{};
+  const int64_t N = p->num_tokens, K = p->num_topk, E = p->num_experts, R = p->num_ranks;
+  const int64_t T = N / R;
+  int64_t C = (512 + K - 1) / K;           // about 512 pairs per block
+  const int64_t C2 = (N + 511) / 512;      // at most ~512 chunks overall
+  if (C2 > C) C = C2;
+  const int64_t CB = T > 0 ? (T + C - 1) / C : 0;
+  pl.C = (int32_t)C;
+  pl.CB = (int32_t)CB;
+  pl.B = (int32_t)(R * CB);
+  int64_t o = 0;
+  pl.o_err = o;
+  o = align256(o + 4);
+  pl.o_cnt = o;
+  o = align256(o + 4 * (int64_t)pl.B * E);
+  pl.o_pre = o;
+  o = align256(o + 4 * (int64_t)pl.B * E);
+  pl.o_rank = o;
+  o = align256(o + 4 * (int64_t)pl.B * R);
+  pl.o_berr = o;
+  o = align256(o + 4 * (int64_t)pl.B);
+  pl.bytes = o;
+  return pl;
+}
+
+template <int NV>
+void launch_dispatch_bf16(dim3 grid, hipStream_t st, const ep_problem_t* p, const void* x,
+                          const float* w, const int32_t* slot_of, const int32_t* off,
+                          const int32_t* cnt, void* recv_x, int32_t* recv_src, float* recv_w,
+                          int64_t cap, int tok_blocks) {
+  dispatch_bf16_kernel<NV><<<grid, kThreads, 0, st>>>(
+      (const u32x4*)x, w, slot_of, off, cnt, (u32x4*)recv_x, recv_src, recv_w, p->num_tokens,
+      p->num_topk, p->num_experts, p->hidden / 8, cap, tok_blocks);
+}
+
+template <int NI>
+void launch_dispatch_fp8(dim3 grid, hipStream_t st, const ep_problem_t* p, const void* x,
+                         const float* w, const int32_t* slot_of, const int32_t* off,
+                         const int32_t* cnt, void* recv_x, float* recv_scales,
+                         int32_t* recv_src, float* recv_w, int64_t cap, int tok_blocks) {
+  dispatch_fp8_kernel<NI><<<grid, kThreads, 0, st>>>(
+      (const u32x4*)x, w, slot_of, off, cnt, (u32x4*)recv_x, recv_scales, recv_src, recv_w,
+      p->num_tokens, p->num_topk, p->num_experts, p->hidden, cap, tok_blocks);
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+extern "C" {
+
+int64_t ep_recv_capacity(const ep_problem_t* p) {
+  if (validate_layout(p) != EP_OK) return -1;
+  return bound_of(p);
+}
+
+int64_t ep_workspace_bytes(const ep_problem_t* p) {
+  if (validate_layout(p) != EP_OK) return -1;
+  return make_plan(p).bytes;
+}
+
+int ep_get_layout(const ep_problem_t* p, const int32_t* topk_idx, int32_t* num_tokens_per_rank,
+                  int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                  int32_t* num_recv_per_expert, int32_t* expert_slot_offset, int32_t* slot_of,
+                  void* workspace, void* stream) {
+  int rc = validate_layout(p);
+  if (rc != EP_OK) return rc;
+  const int N = p->num_tokens;
+  if (!num_tokens_per_rank || !num_tokens_per_expert || !num_recv_per_expert ||
+      !expert_slot_offset || !workspace)
+    return EP_ERR_INVALID_ARG;
+  if (N > 0 && (!topk_idx || !is_token_in_rank || !slot_of)) return EP_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return EP_ERR_INVALID_ARG;
+  rc = check_device();
+  if (rc != EP_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const Plan pl = make_plan(p);
+  const int K = p->num_topk, E = p->num_experts, R = p->num_ranks;
+  const int T = N / R, L = E / R;
+  char* ws = (char*)workspace;
+  int32_t* err = (int32_t*)(ws + pl.o_err);
+  int32_t* blk_cnt = (int32_t*)(ws + pl.o_cnt);
+  int32_t* blk_pre = (int32_t*)(ws + pl.o_pre);
+  int32_t* blk_rank = (int32_t*)(ws + pl.o_rank);
+  int32_t* blk_err = (int32_t*)(ws + pl.o_berr);
+  EP_LOG("layout N=%d K=%d E=%d R=%d A=%d: blocks=%d chunk=%d tokens", N, K, E, R,
+         p->expert_alignment, pl.B, pl.C);
+  if (pl.B > 0) {
+    layout_count_kernel<<<pl.B, kThreads, 0, st>>>(topk_idx, is_token_in_rank, blk_cnt, blk_rank,
+                                                   blk_err, K, E, R, L, T, pl.CB, pl.C);
+    if ((rc = check_launch("layout_count")) != EP_OK) return rc;
+  }
+  layout_scan_kernel<<<1, kScanThreads, 0, st>>>(blk_cnt, blk_pre, blk_rank, blk_err, err,
+                                                 num_tokens_per_rank, num_tokens_per_expert,
+                                                 num_recv_per_expert, expert_slot_offset, pl.B,
+                                                 pl.CB, E, R, p->expert_alignment);
+  if ((rc = check_launch("layout_scan")) != EP_OK) return rc;
+  if (pl.B > 0) {
+    layout_assign_kernel<<<pl.B, kThreads, 0, st>>>(topk_idx, blk_pre, expert_slot_offset,
+                                                    slot_of, K, E, T, pl.CB, pl.C);
+    if ((rc = check_launch("layout_assign")) != EP_OK) return rc;
+  }
+  return EP_OK;
+}
+
+int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
+                const int32_t* slot_of, const int32_t* expert_slot_offset,
+                const int32_t* num_recv_per_expert, void* recv_x, float* recv_scales,
+                int32_t* recv_src_idx, float* recv_topk_weights, int64_t recv_capacity,
+                void* stream) {
+  int rc = validate_payload(p);
+  if (rc != EP_OK) return rc;
+  if (recv_capacity < bound_of(p)) return EP_ERR_CAPACITY;
+  const int N = p->num_tokens;
+  const bool meta = recv_src_idx || recv_topk_weights;
+  if (recv_topk_weights && N > 0 && !topk_weights) return EP_ERR_INVALID_ARG;
+  if (N > 0 && (!x || !slot_of || !recv_x)) return EP_ERR_INVALID_ARG;
+  if (p->use_fp8 && N > 0 && !recv_scales) return EP_ERR_INVALID_ARG;
+  if (meta && recv_capacity > 0 && (!expert_slot_offset || !num_recv_per_expert))
+    return EP_ERR_INVALID_ARG;
+  rc = check_device();
+  if (rc != EP_OK) return rc;
+  const int tok_blocks = (N + kWaves - 1) / kWaves;
+  const int64_t fill_blocks64 = meta ? (recv_capacity + kFillSlots - 1) / kFillSlots : 0;
+  if (fill_blocks64 + tok_blocks > INT32_MAX) return EP_ERR_INVALID_ARG;
+  const int grid = tok_blocks + (int)fill_blocks64;
+  if (grid == 0) return EP_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const int H = p->hidden;
+  if (!p->use_fp8) {
+    const int q = (H / 8 + 63) / 64;
+    EP_LOG("dispatch bf16 N=%d H=%d K=%d cap=%lld: token blocks=%d fill blocks=%lld nv=%d", N, H,
+           p->num_topk, (long long)recv_capacity, tok_blocks, (long long)fill_blocks64, q);
+#define EP_D16(NV)                                                                          \
+  launch_dispatch_bf16<NV>(grid, st, p, x, topk_weights, slot_of, expert_slot_offset,      \
+                           num_recv_per_expert, recv_x, recv_src_idx, recv_topk_weights,   \
+                           recv_capacity, tok_blocks)
+    if (q <= 1) EP_D16(1);
+    else if (q <= 2) EP_D16(2);
+    else if (q <= 4) EP_D16(4);
+    else if (q <= 8) EP_D16(8);
+    else if (q <= 14) EP_D16(14);
+    else EP_D16(16);
+#undef EP_D16
+  } else {
+    const int q = (H + 1023) / 1024;
+    EP_LOG("dispatch e4m3 N=%d H=%d K=%d cap=%lld: token blocks=%d fill blocks=%lld ni=%d", N, H,
+           p->num_topk, (long long)recv_capacity, tok_blocks, (long long)fill_blocks64, q);
+#define EP_D8(NI)                                                                           \
+  launch_dispatch_fp8<NI>(grid, st, p, x, topk_weights, slot_of, expert_slot_offset,       \
+                          num_recv_per_expert, recv_x, recv_scales, recv_src_idx,          \
+                          recv_topk_weights, recv_capacity, tok_blocks)
+    if (q <= 1) EP_D8(1);
+    else if (q <= 2) EP_D8(2);
+    else if (q <= 4) EP_D8(4);
+    else if (q <= 7) EP_D8(7);
+    else EP_D8(8);
+#undef EP_D8
+  }
+  return check_launch("dispatch");
+}
+
+int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slot_of,
+               const float* topk_weights, void* y, int64_t recv_capacity, void* stream) {
+  int rc = validate_payload(p);
+  if (rc != EP_OK) return rc;
+  const int N = p->num_tokens;
+  if (recv_capacity < 0) return EP_ERR_INVALID_ARG;
+  if (N == 0) return EP_OK;
+  if (!slot_of || !topk_weights || !y || (recv_capacity > 0 && !expert_out))
+    return EP_ERR_INVALID_ARG;
+  rc = check_device();
+  if (rc != EP_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int blocks = (N + kWaves - 1) / kWaves;
+  EP_LOG("combine N=%d H=%d K=%d cap=%lld: blocks=%d nv=%d", N, p->hidden, p->num_topk,
+         (long long)recv_capacity, blocks, EP_COMBINE_NV);
+  combine_kernel<EP_COMBINE_NV><<<blocks, kThreads, 0, st>>>(
+      (const u32x4*)expert_out, slot_of, topk_weights, (u32x4*)y, N, p->num_topk, p->hidden / 8,
+      recv_capacity);
+  return check_launch("combine");
+}
+
+int ep_layout_error(const void* workspace, int32_t* flags, void* stream) {
+  if (!workspace || !flags) return EP_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof v, hipMemcpyDeviceToHost, st) != hipSuccess)
+    return EP_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return EP_ERR_HIP;
+  *flags = v;
+  return EP_OK;
+}
+
+const char* ep_status_str(int status) {
+  switch (status) {
+    case EP_OK: return "ok";
+    case EP_ERR_INVALID_ARG: return "invalid argument";
+    case EP_ERR_CAPACITY: return "receive capacity below N*K + E*(A-1)";
+    case EP_ERR_HIP: return "HIP error";
+    case EP_ERR_UNSUPPORTED: return "device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

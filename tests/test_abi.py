@@ -1,0 +1,114 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/ep_get.h declares, and its host-only entry points (capacity,
+workspace sizing, status strings, argument validation) behave as documented.
+No call here reaches a kernel launch: each one is rejected by host validation
+first or is host-only by contract.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_ep_get_amd as ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep_get.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ("ep_get_layout", "ep_dispatch", "ep_combine", "ep_recv_capacity",
+               "ep_workspace_bytes", "ep_layout_error", "ep_status_str"):
+        assert fn in names
+    assert set(names) == set(ep.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(ep.LIB_PATH), "build the library first (__graft_entry__.build())"
+    L = ctypes.CDLL(ep.LIB_PATH)
+    for fn in declared_functions():
+        assert hasattr(L, fn), fn
+    out = os.popen(f"nm -D --defined-only {ep.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT (ep_[a-z_]+)\b", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_capacity_and_workspace():
+    # N*K + E*(A-1)
+    assert ep.recv_capacity(4096, 8, 256, 8, 128) == 4096 * 8 + 256 * 127
+    assert ep.recv_capacity(128, 2, 16, 4, 1) == 256
+    assert ep.recv_capacity(0, 8, 256, 8, 128) == 256 * 127
+    ws = ep.workspace_bytes(4096, 8, 256, 8, 128)
+    assert ws > 0 and ws % 256 == 0
+    assert ep.workspace_bytes(0, 8, 256, 8, 1) >= 256
+    with pytest.raises(ValueError):
+        ep.recv_capacity(10, 8, 256, 8, 1)        # N % R != 0
+    with pytest.raises(ValueError):
+        ep.recv_capacity(16, 8, 250, 8, 1)        # E % R != 0
+    with pytest.raises(ValueError):
+        ep.recv_capacity(16, 33, 256, 8, 1)       # K too large
+    with pytest.raises(ValueError):
+        ep.recv_capacity(16, 8, 2048, 8, 1)       # E too large
+    with pytest.raises(ValueError):
+        ep.recv_capacity(2 ** 28, 16, 256, 8, 1)  # bound beyond int32
+
+
+def test_status_strings():
+    L = ep.lib()
+    for code in range(5):
+        assert L.ep_status_str(code)
+    assert b"unknown" in L.ep_status_str(99)
+
+
+def _p(**kw):
+    base = dict(num_tokens=16, hidden=256, num_topk=2, num_experts=16, num_ranks=4,
+                expert_alignment=1, use_fp8=False)
+    base.update(kw)
+    return ep.problem(**base)
+
+
+BAD = [dict(num_tokens=-1), dict(num_topk=0), dict(num_topk=33), dict(num_experts=0),
+       dict(num_experts=1025), dict(num_ranks=0), dict(num_ranks=32, num_experts=16),
+       dict(num_experts=18), dict(num_tokens=18), dict(expert_alignment=0)]
+
+
+@pytest.mark.parametrize("kw", BAD, ids=[str(b) for b in BAD])
+def test_layout_rejects_bad_descriptors(kw):
+    L = ep.lib()
+    p = _p(**kw)
+    fake = ctypes.c_void_p(256)   # never dereferenced: validation runs first
+    rc = L.ep_get_layout(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, None)
+    assert rc == 1
+
+
+def test_payload_rejects_bad_descriptors():
+    L = ep.lib()
+    fake = ctypes.c_void_p(256)
+    for kw in (dict(hidden=0), dict(hidden=12), dict(hidden=200, use_fp8=True)):
+        p = _p(**kw)
+        assert L.ep_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
+                             fake, 10 ** 6, None) == 1
+        assert L.ep_combine(ctypes.byref(p), fake, fake, fake, fake, 10 ** 6, None) == 1
+    p = _p()
+    # capacity below N*K + E*(A-1)
+    assert L.ep_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                         16 * 2 - 1, None) == 2
+    # missing pointers
+    assert L.ep_dispatch(ctypes.byref(p), None, fake, fake, fake, fake, fake, None, fake, fake,
+                         10 ** 6, None) == 1
+    assert L.ep_combine(ctypes.byref(p), fake, None, fake, fake, 10 ** 6, None) == 1
+    # fp8 needs a scale buffer
+    p8 = _p(use_fp8=True)
+    assert L.ep_dispatch(ctypes.byref(p8), fake, fake, fake, fake, fake, fake, None, fake, fake,
+                         10 ** 6, None) == 1
+    # workspace must be 256-byte aligned
+    assert L.ep_get_layout(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake,
+                           ctypes.c_void_p(260), None) == 1
+    assert L.ep_layout_error(None, None, None) == 1
