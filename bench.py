@@ -90,17 +90,21 @@ def cpu_baseline(w, inp, eo_bits, budget_s):
 
 
 def ceilings(nbytes=1 << 30):
-    """Measured HBM copy and pure-write bandwidth (GB/s) on this GPU."""
+    """Measured HBM copy, pure-write and pure-read bandwidth (GB/s) on this GPU."""
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "combine_ep_get_amd", "_lib", "libepceil.so"))
     lib.epc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.epc_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    lib.epc_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    a = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(256, dtype=torch.int32, device="cuda")
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     res = {}
-    for name, fn, moved in (("copy", lambda: lib.epc_copy(b.data_ptr(), a.data_ptr(), nbytes, st), 2),
-                            ("write", lambda: lib.epc_write(a.data_ptr(), nbytes, 7, st), 1)):
+    for name, fn, moved in (
+            ("copy", lambda: lib.epc_copy(b.data_ptr(), a.data_ptr(), nbytes, st), 2),
+            ("write", lambda: lib.epc_write(a.data_ptr(), nbytes, 7, st), 1),
+            ("read", lambda: lib.epc_read(a.data_ptr(), nbytes, sink.data_ptr(), st), 1)):
         for _ in range(3):
             assert fn() == 0
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -166,20 +170,30 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
           flush=True)
+    # The timed region: K back-to-back steps, nothing else enqueued between them.
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    g0.record()
     for i in range(args.steps):
-        step(events[i])
+        step()
+    g1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
+    gpu_step_ms = g0.elapsed_time(g1) / args.steps
+    # Per-kernel durations: the same steps again, with an event between kernels
+    # (each event record costs a few microseconds of queue time, so these steps
+    # are not the ones the headline number comes from).
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
     lay_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     dis_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     com_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
-    ev_step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
 
     disp_b, comb_b = algorithmic_bytes(w)
     total_b = disp_b + comb_b
@@ -215,12 +229,14 @@ def main():
         "tokens_per_s": round(w.N / step_s, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": total_b,
+        "gpu_ms_per_step": round(gpu_step_ms, 4),
         "kernel_ms": {"layout": round(float(lay_ms.mean()), 4),
                       "dispatch": round(float(dis_ms.mean()), 4),
                       "combine": round(float(com_ms.mean()), 4),
-                      "step_events": round(float(ev_step_ms.mean()), 4),
-                      "step_events_p10": round(float(np.percentile(ev_step_ms, 10)), 4),
-                      "step_events_p90": round(float(np.percentile(ev_step_ms, 90)), 4)},
+                      "dispatch_p10": round(float(np.percentile(dis_ms, 10)), 4),
+                      "dispatch_p90": round(float(np.percentile(dis_ms, 90)), 4),
+                      "combine_p10": round(float(np.percentile(com_ms, 10)), 4),
+                      "combine_p90": round(float(np.percentile(com_ms, 90)), 4)},
         "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},

@@ -52,24 +52,37 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -c 'import __graft_entry__ as g; g.build()'`")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i64, P = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(Problem)
-        L.ep_recv_capacity.restype = i64
-        L.ep_recv_capacity.argtypes = [P]
-        L.ep_workspace_bytes.restype = i64
-        L.ep_workspace_bytes.argtypes = [P]
-        L.ep_get_layout.restype = ctypes.c_int
-        L.ep_get_layout.argtypes = [P] + [vp] * 9
-        L.ep_dispatch.restype = ctypes.c_int
-        L.ep_dispatch.argtypes = [P] + [vp] * 9 + [i64, vp]
-        L.ep_combine.restype = ctypes.c_int
-        L.ep_combine.argtypes = [P, vp, vp, vp, vp, i64, vp]
-        L.ep_layout_error.restype = ctypes.c_int
-        L.ep_layout_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
-        L.ep_status_str.restype = ctypes.c_char_p
-        L.ep_status_str.argtypes = [ctypes.c_int]
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+def use_library(path):
+    """Route every later call to the build of the library at ``path`` (a
+    build of the same sources with other compile-time launch parameters)."""
+    global _lib
+    _lib = load(path)
+    return _lib
+
+
+def load(path):
+    """Open a build of libepget.so and declare its C signatures."""
+    L = ctypes.CDLL(path)
+    vp, i64, P = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(Problem)
+    L.ep_recv_capacity.restype = i64
+    L.ep_recv_capacity.argtypes = [P]
+    L.ep_workspace_bytes.restype = i64
+    L.ep_workspace_bytes.argtypes = [P]
+    L.ep_get_layout.restype = ctypes.c_int
+    L.ep_get_layout.argtypes = [P] + [vp] * 9
+    L.ep_dispatch.restype = ctypes.c_int
+    L.ep_dispatch.argtypes = [P] + [vp] * 9 + [i64, vp]
+    L.ep_combine.restype = ctypes.c_int
+    L.ep_combine.argtypes = [P, vp, vp, vp, vp, i64, vp]
+    L.ep_layout_error.restype = ctypes.c_int
+    L.ep_layout_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
+    L.ep_status_str.restype = ctypes.c_char_p
+    L.ep_status_str.argtypes = [ctypes.c_int]
+    return L
 
 
 def problem(num_tokens, hidden, num_topk, num_experts, num_ranks, expert_alignment=1,

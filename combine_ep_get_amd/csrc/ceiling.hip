@@ -36,9 +36,34 @@ __global__ __launch_bounds__(kThreads) void write_kernel(u32x4* __restrict__ dst
     if (j < n16) __builtin_nontemporal_store(v, dst + j);
   }
 }
+__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ src,
+                                                        int64_t n16, uint32_t* __restrict__ sink) {
+  const int64_t base = ((int64_t)blockIdx.x * kThreads * kPer) + threadIdx.x;
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int64_t j = base + (int64_t)i * kThreads;
+    if (j < n16) {
+      const u32x4 v = __builtin_nontemporal_load(src + j);
+      x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  }
+  if (x == 0x9E3779B9u) sink[threadIdx.x] = x;   // keeps the loads; practically never stores
+}
 }  // namespace
 
 extern "C" {
+// Read `bytes` (multiple of 16, 16-byte aligned); `sink` must hold 256 uint32.
+int epc_read(const void* src, int64_t bytes, void* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 || (uintptr_t)src % 16) return 1;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = (n16 + kThreads * kPer - 1) / (kThreads * kPer);
+  if (blocks == 0) return 0;
+  read_kernel<<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src, n16,
+                                                                      (uint32_t*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
 // Copy `bytes` (multiple of 16, 16-byte aligned pointers) from src to dst.
 int epc_copy(void* dst, const void* src, int64_t bytes, void* stream) {
   if (bytes < 0 || bytes % 16 || ((uintptr_t)dst | (uintptr_t)src) % 16) return 1;

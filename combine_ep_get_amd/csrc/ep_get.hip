@@ -50,12 +50,17 @@
 #ifndef EP_COMBINE_NV
 #define EP_COMBINE_NV 2
 #endif
+#ifndef EP_COMBINE_TPT
+#define EP_COMBINE_TPT 64
+#endif
+#ifndef EP_DISPATCH_TPT
+#define EP_DISPATCH_TPT 64
+#endif
 
 namespace {
 
 constexpr int kThreads = 256;             // 4 wavefronts per block
 constexpr int kWaves = kThreads / 64;
-constexpr int kScanThreads = 1024;
 constexpr int kFillPerThread = 8;         // padding-fill: slots per thread
 constexpr int kFillSlots = kThreads * kFillPerThread;
 
@@ -135,7 +140,7 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
 // tokens (the last chunk of a source may be shorter).
 struct Plan {
   int32_t C, CB, B;
-  int64_t o_err, o_cnt, o_pre, o_rank, o_berr, bytes;
+  int64_t o_err, o_cnt, o_rank, o_berr, bytes;
 };
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
@@ -185,92 +190,31 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(
   if (tid == 0) blk_err[b] = err;
 }
 
-// Phase 2 (one block): per-expert exclusive prefix over blocks, receive
-// counts, padded exclusive scan over experts, per-source matrices, error word.
-__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
-    const int32_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_pre,
+// Phase 2: scan and stable slots.  Every block first rebuilds, from the
+// per-block histograms of phase 1, what it needs of the device-wide scan:
+// its own exclusive prefix over earlier blocks for each expert and the
+// per-expert totals, whose padded exclusive scan gives the region offsets
+// (redundant per block, but all loads are independent and in flight together,
+// which is cheaper than a serial single-block scan plus another launch).
+// Block 0 publishes the offsets, receive counts and error word; the first
+// block of each source publishes that source's rows of the count matrices.
+//
+// Slots: pairs are taken in (token, k) order, 256 per round; within a
+// wavefront each lane ORs its bit into the 64-bit LDS mask of its expert, so
+// the rank among equal experts is the popcount of the lower lanes' bits, plus
+// the counts of lower wavefronts, plus everything the block and the earlier
+// blocks already placed for that expert.
+constexpr int kEPerThread = EP_MAX_EXPERTS / kThreads;  // experts per thread in the scan
+
+__global__ __launch_bounds__(kThreads) void layout_assign_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_cnt,
     const int32_t* __restrict__ blk_rank, const int32_t* __restrict__ blk_err,
     int32_t* __restrict__ err_word, int32_t* __restrict__ num_tokens_per_rank,
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_recv,
-    int32_t* __restrict__ off, int B, int CB, int E, int R, int A) {
-  __shared__ int part[kScanThreads];
-  __shared__ int wsum[kScanThreads / 64];
-  const int tid = threadIdx.x;
-  const int S = kScanThreads / E;  // block slices per expert (E <= 1024)
-  const int e = tid % E, sl = tid / E;
-  const bool act = sl < S;
-  const int b0 = (int)((int64_t)B * sl / S), b1 = (int)((int64_t)B * (sl + 1) / S);
-  int sum = 0;
-  if (act)
-    for (int b = b0; b < b1; b++) sum += blk_cnt[(int64_t)b * E + e];
-  if (act) part[sl * E + e] = sum;
-  __syncthreads();
-  int tot = 0;
-  if (act) {
-    int pre = 0;
-    for (int s2 = 0; s2 < S; s2++) {
-      int v = part[s2 * E + e];
-      if (s2 < sl) pre += v;
-      tot += v;
-    }
-    for (int b = b0; b < b1; b++) {
-      int v = blk_cnt[(int64_t)b * E + e];
-      blk_pre[(int64_t)b * E + e] = pre;
-      pre += v;
-    }
-    if (sl == 0) num_recv[e] = tot;
-  }
-  // padded sizes: thread tid < E is (expert tid, slice 0) and holds its total
-  int x = (tid < E) ? (tot + A - 1) / A * A : 0;
-  const int lane = tid & 63, w = tid >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wsum[w] = x;
-  __syncthreads();
-  if (tid < 64) {
-    int v = (tid < kScanThreads / 64) ? wsum[tid] : 0;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      int y = __shfl_up(v, d);
-      if (tid >= d) v += y;
-    }
-    if (tid < kScanThreads / 64) wsum[tid] = v;
-  }
-  __syncthreads();
-  if (w > 0) x += wsum[w - 1];
-  if (tid < E) off[tid + 1] = x;
-  if (tid == 0) off[0] = 0;
-  for (int q = tid; q < R * E; q += kScanThreads) {
-    const int s = q / E, ex = q % E;
-    int v = 0;
-    for (int b = s * CB; b < (s + 1) * CB; b++) v += blk_cnt[(int64_t)b * E + ex];
-    num_tokens_per_expert[q] = v;
-  }
-  for (int q = tid; q < R * R; q += kScanThreads) {
-    const int s = q / R, r = q % R;
-    int v = 0;
-    for (int b = s * CB; b < (s + 1) * CB; b++) v += blk_rank[(int64_t)b * R + r];
-    num_tokens_per_rank[q] = v;
-  }
-  int ev = 0;
-  for (int b = tid; b < B; b += kScanThreads) ev |= blk_err[b];
-  ev = __syncthreads_or(ev);
-  if (tid == 0) *err_word = ev ? EP_LAYOUT_ERR_INDEX : 0;
-}
-
-// Phase 3: stable slot of every pair.  Pairs are taken in (token, k) order,
-// 256 per round; within a wavefront each lane ORs its bit into the 64-bit LDS
-// mask of its expert, so the rank among equal experts is the popcount of the
-// lower lanes' bits, plus the counts of lower wavefronts, plus everything the
-// block and the earlier blocks of the same expert already placed.
-__global__ __launch_bounds__(kThreads) void layout_assign_kernel(
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_pre,
-    const int32_t* __restrict__ off, int32_t* __restrict__ slot_of, int K, int E, int T,
-    int CB, int C) {
+    int32_t* __restrict__ off, int32_t* __restrict__ slot_of, int K, int E, int R, int T,
+    int CB, int C, int B, int A) {
   __shared__ int base[EP_MAX_EXPERTS];
+  __shared__ int wsum[kWaves];
   __shared__ unsigned long long masks[kWaves][EP_MAX_EXPERTS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x, src = b / CB, c = b % CB;
@@ -278,17 +222,113 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
   const int t1 = src * T + min((c + 1) * C, T);
   const int64_t p0 = (int64_t)t0 * K;
   const int np = (t1 - t0) * K;
-  for (int e = tid; e < E; e += kThreads) {
-    base[e] = off[e] + blk_pre[(int64_t)b * E + e];
+  const int e_first = (tid < np) ? topk_idx[p0 + tid] : -1;  // round 0, loaded early
+
+  // (a) per-expert prefix over blocks < b, totals, and this source's row
+  int pre[kEPerThread], tot[kEPerThread], srow[kEPerThread];
+#pragma unroll
+  for (int j = 0; j < kEPerThread; j++) {
+    pre[j] = 0;
+    tot[j] = 0;
+    srow[j] = 0;
+  }
+  const int s0 = src * CB, s1 = s0 + CB;
+#pragma unroll
+  for (int j = 0; j < kEPerThread; j++) {
+    const int e = tid + j * kThreads;
+    if (e >= E) break;
+    int bb = 0;
+    for (; bb + 16 <= B; bb += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; u++) v[u] = blk_cnt[(int64_t)(bb + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; u++) {
+        const int bi = bb + u;
+        tot[j] += v[u];
+        if (bi < b) pre[j] += v[u];
+        if (bi >= s0 && bi < s1) srow[j] += v[u];
+      }
+    }
+    for (; bb < B; bb++) {
+      const int v = blk_cnt[(int64_t)bb * E + e];
+      tot[j] += v;
+      if (bb < b) pre[j] += v;
+      if (bb >= s0 && bb < s1) srow[j] += v;
+    }
+  }
+  // (b) padded exclusive scan over experts: thread tid owns experts
+  //     tid, tid+256, ...; scan in expert order via LDS
+#pragma unroll
+  for (int j = 0; j < kEPerThread; j++) {
+    const int e = tid + j * kThreads;
+    if (e < E) base[e] = (tot[j] + A - 1) / A * A;
+  }
+  __syncthreads();
+  // each thread sums a run of kEPerThread consecutive experts, then a block scan
+  int run[kEPerThread];
+  int acc = 0;
+#pragma unroll
+  for (int j = 0; j < kEPerThread; j++) {
+    const int e = tid * kEPerThread + j;
+    run[j] = (e < E) ? base[e] : 0;
+    acc += run[j];
+  }
+  int x = acc;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int wpre = 0;
+  for (int ww = 0; ww < w; ww++) wpre += wsum[ww];
+  int excl = wpre + x - acc;  // exclusive prefix of this thread's run
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kEPerThread; j++) {
+    const int e = tid * kEPerThread + j;
+    if (e < E) base[e] = excl;  // base[e] now holds off[e]
+    excl += run[j];
+  }
+  if (b == 0 && tid == kThreads - 1) off[E] = excl;
+  __syncthreads();
+  // (c) publish, then turn base[] into this block's first slot per expert
+#pragma unroll
+  for (int j = 0; j < kEPerThread; j++) {
+    const int e = tid + j * kThreads;
+    if (e >= E) break;
+    if (b == 0) {
+      off[e] = base[e];
+      num_recv[e] = tot[j];
+    }
+    if (c == 0) num_tokens_per_expert[(int64_t)src * E + e] = srow[j];
+    base[e] += pre[j];
 #pragma unroll
     for (int ww = 0; ww < kWaves; ww++) masks[ww][e] = 0ull;
   }
+  if (c == 0) {
+    for (int r = tid; r < R; r += kThreads) {
+      int v = 0;
+      for (int bb = s0; bb < s1; bb++) v += blk_rank[(int64_t)bb * R + r];
+      num_tokens_per_rank[(int64_t)src * R + r] = v;
+    }
+  }
+  if (b == 0) {
+    int ev = 0;
+    for (int bb = tid; bb < B; bb += kThreads) ev |= blk_err[bb];
+    ev = __syncthreads_or(ev);
+    if (tid == 0) *err_word = ev ? EP_LAYOUT_ERR_INDEX : 0;
+  }
   __syncthreads();
+
+  // (d) stable ranks
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int r0 = 0; r0 < np; r0 += kThreads) {
     const int p = r0 + tid;
-    int e = -1;
-    if (p < np) e = topk_idx[p0 + p];
+    int e = e_first;
+    if (r0 > 0) e = (p < np) ? topk_idx[p0 + p] : -1;
     const bool ok = (e >= 0 && e < E);
     if (ok) atomicOr(&masks[w][e], 1ull << lane);
     __syncthreads();
@@ -296,9 +336,9 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     unsigned long long m = 0;
     if (ok) {
       m = masks[w][e];
-      int pre = 0;
-      for (int w2 = 0; w2 < w; w2++) pre += __popcll(masks[w2][e]);
-      slot = base[e] + pre + __popcll(m & below);
+      int pw = 0;
+      for (int w2 = 0; w2 < w; w2++) pw += __popcll(masks[w2][e]);
+      slot = base[e] + pw + __popcll(m & below);
     }
     __syncthreads();
     if (ok && (m & below) == 0ull) {  // lowest lane of this expert in this wave
@@ -308,6 +348,21 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     __syncthreads();
     if (p < np) slot_of[p0 + p] = slot;
   }
+}
+
+// N == 0: no blocks of the two kernels above run; publish zero outputs.
+__global__ __launch_bounds__(kThreads) void layout_empty_kernel(
+    int32_t* __restrict__ err_word, int32_t* __restrict__ num_tokens_per_rank,
+    int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_recv,
+    int32_t* __restrict__ off, int E, int R) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += kThreads) {
+    off[e] = 0;
+    if (e < E) num_recv[e] = 0;
+  }
+  for (int q = tid; q < R * E; q += kThreads) num_tokens_per_expert[q] = 0;
+  for (int q = tid; q < R * R; q += kThreads) num_tokens_per_rank[q] = 0;
+  if (tid == 0) *err_word = 0;
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -366,8 +421,10 @@ __device__ __forceinline__ void write_meta(int t, int K, int lane, int myslot,
   }
 }
 
-// bf16 rows: one wavefront per token; NV 16-byte chunks per lane per pass.
-template <int NV>
+// bf16 rows: TPT threads (a multiple of 64) per token; NV 16-byte chunks per
+// thread per pass, so one pass moves TPT*NV*16 bytes of the row, which is read
+// once into VGPRs and then stored to each of the token's K slots.
+template <int TPT, int NV>
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
     const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
@@ -379,16 +436,18 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     fill_padding(blockIdx.x - tok_blocks, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
     return;
   }
-  const int t = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  constexpr int kTok = kThreads / TPT;
+  const int t = uniform(blockIdx.x * kTok + (int)(threadIdx.x / TPT));
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
+  const int vl = threadIdx.x % TPT;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
   const u32x4* row = x + (int64_t)t * H8;
-  for (int base = 0; base < H8; base += 64 * NV) {
+  for (int base = 0; base < H8; base += TPT * NV) {
     u32x4 v[NV];
 #pragma unroll
     for (int i = 0; i < NV; i++) {
-      const int c = base + i * 64 + lane;
+      const int c = base + i * TPT + vl;
       if (c < H8) v[i] = ld16(row + c);
     }
     for (int k = 0; k < K; k++) {
@@ -397,12 +456,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
       u32x4* dst = recv_x + (int64_t)s * H8;
 #pragma unroll
       for (int i = 0; i < NV; i++) {
-        const int c = base + i * 64 + lane;
+        const int c = base + i * TPT + vl;
         if (c < H8) st16(dst + c, v[i]);
       }
     }
   }
-  write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+  if (vl < 64) write_meta(t, K, lane, myslot, w, recv_src, recv_w);
 }
 
 // e4m3 rows: one wavefront per token.  A lane owns 16 consecutive channels
@@ -495,20 +554,23 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
 }
 
 // ---------------------------------------------------------------- combine
-// One wavefront per token.  For each pass of NV 16-byte chunks per lane, the
-// rows of up to 8 pairs are loaded first (all in flight), then accumulated in
-// ascending k: acc = acc + w_k * row_k (separately rounded mul and add).
-template <int NV>
+// TPT threads (a multiple of 64) per token.  For each pass of NV 16-byte
+// chunks per thread, the rows of up to 8 pairs are loaded first (all in
+// flight), then accumulated in ascending k: acc = acc + w_k * row_k
+// (separately rounded multiply and add), and stored as bf16 (RNE).
+template <int TPT, int NV>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const u32x4* __restrict__ eo, const int32_t* __restrict__ slot_of,
     const float* __restrict__ w, u32x4* __restrict__ y, int N, int K, int H8, int64_t cap) {
-  const int t = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  constexpr int kTok = kThreads / TPT;
+  const int t = uniform(blockIdx.x * kTok + (int)(threadIdx.x / TPT));
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
+  const int vl = threadIdx.x % TPT;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
   const float myw = (lane < K) ? w[(int64_t)t * K + lane] : 0.0f;
   u32x4* yrow = y + (int64_t)t * H8;
-  for (int base = 0; base < H8; base += 64 * NV) {
+  for (int base = 0; base < H8; base += TPT * NV) {
     float acc[NV][8];
 #pragma unroll
     for (int i = 0; i < NV; i++)
@@ -524,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
           const u32x4* r = eo + (int64_t)s * H8;
 #pragma unroll
           for (int i = 0; i < NV; i++) {
-            const int c = base + i * 64 + lane;
+            const int c = base + i * TPT + vl;
             if (c < H8) v[j][i] = ld16(r + c);
           }
         }
@@ -546,7 +608,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     }
 #pragma unroll
     for (int i = 0; i < NV; i++) {
-      const int c = base + i * 64 + lane;
+      const int c = base + i * TPT + vl;
       if (c < H8) {
         u32x4 o;
 #pragma unroll
@@ -629,8 +691,9 @@ Plan make_plan(const ep_problem_t* p) {
   Plan pl{};
   const int64_t N = p->num_tokens, K = p->num_topk, E = p->num_experts, R = p->num_ranks;
   const int64_t T = N / R;
-  int64_t C = (512 + K - 1) / K;           // about 512 pairs per block
-  const int64_t C2 = (N + 511) / 512;      // at most ~512 chunks overall
+  // at least ~512 pairs per block, and about 64 blocks when N*K is larger
+  int64_t C = (512 + K - 1) / K;
+  const int64_t C2 = (N * K / 64 + K - 1) / K;
   if (C2 > C) C = C2;
   const int64_t CB = T > 0 ? (T + C - 1) / C : 0;
   pl.C = (int32_t)C;
@@ -640,8 +703,6 @@ Plan make_plan(const ep_problem_t* p) {
   pl.o_err = o;
   o = align256(o + 4);
   pl.o_cnt = o;
-  o = align256(o + 4 * (int64_t)pl.B * E);
-  pl.o_pre = o;
   o = align256(o + 4 * (int64_t)pl.B * E);
   pl.o_rank = o;
   o = align256(o + 4 * (int64_t)pl.B * R);
@@ -656,7 +717,7 @@ void launch_dispatch_bf16(dim3 grid, hipStream_t st, const ep_problem_t* p, cons
                           const float* w, const int32_t* slot_of, const int32_t* off,
                           const int32_t* cnt, void* recv_x, int32_t* recv_src, float* recv_w,
                           int64_t cap, int tok_blocks) {
-  dispatch_bf16_kernel<NV><<<grid, kThreads, 0, st>>>(
+  dispatch_bf16_kernel<EP_DISPATCH_TPT, NV><<<grid, kThreads, 0, st>>>(
       (const u32x4*)x, w, slot_of, off, cnt, (u32x4*)recv_x, recv_src, recv_w, p->num_tokens,
       p->num_topk, p->num_experts, p->hidden / 8, cap, tok_blocks);
 }
@@ -707,26 +768,23 @@ int ep_get_layout(const ep_problem_t* p, const int32_t* topk_idx, int32_t* num_t
   char* ws = (char*)workspace;
   int32_t* err = (int32_t*)(ws + pl.o_err);
   int32_t* blk_cnt = (int32_t*)(ws + pl.o_cnt);
-  int32_t* blk_pre = (int32_t*)(ws + pl.o_pre);
   int32_t* blk_rank = (int32_t*)(ws + pl.o_rank);
   int32_t* blk_err = (int32_t*)(ws + pl.o_berr);
   EP_LOG("layout N=%d K=%d E=%d R=%d A=%d: blocks=%d chunk=%d tokens", N, K, E, R,
          p->expert_alignment, pl.B, pl.C);
-  if (pl.B > 0) {
-    layout_count_kernel<<<pl.B, kThreads, 0, st>>>(topk_idx, is_token_in_rank, blk_cnt, blk_rank,
-                                                   blk_err, K, E, R, L, T, pl.CB, pl.C);
-    if ((rc = check_launch("layout_count")) != EP_OK) return rc;
+  if (pl.B == 0) {
+    layout_empty_kernel<<<1, kThreads, 0, st>>>(err, num_tokens_per_rank, num_tokens_per_expert,
+                                                num_recv_per_expert, expert_slot_offset, E, R);
+    return check_launch("layout_empty");
   }
-  layout_scan_kernel<<<1, kScanThreads, 0, st>>>(blk_cnt, blk_pre, blk_rank, blk_err, err,
-                                                 num_tokens_per_rank, num_tokens_per_expert,
-                                                 num_recv_per_expert, expert_slot_offset, pl.B,
-                                                 pl.CB, E, R, p->expert_alignment);
-  if ((rc = check_launch("layout_scan")) != EP_OK) return rc;
-  if (pl.B > 0) {
-    layout_assign_kernel<<<pl.B, kThreads, 0, st>>>(topk_idx, blk_pre, expert_slot_offset,
-                                                    slot_of, K, E, T, pl.CB, pl.C);
-    if ((rc = check_launch("layout_assign")) != EP_OK) return rc;
-  }
+  layout_count_kernel<<<pl.B, kThreads, 0, st>>>(topk_idx, is_token_in_rank, blk_cnt, blk_rank,
+                                                 blk_err, K, E, R, L, T, pl.CB, pl.C);
+  if ((rc = check_launch("layout_count")) != EP_OK) return rc;
+  layout_assign_kernel<<<pl.B, kThreads, 0, st>>>(
+      topk_idx, blk_cnt, blk_rank, blk_err, err, num_tokens_per_rank, num_tokens_per_expert,
+      num_recv_per_expert, expert_slot_offset, slot_of, K, E, R, T, pl.CB, pl.C, pl.B,
+      p->expert_alignment);
+  if ((rc = check_launch("layout_assign")) != EP_OK) return rc;
   return EP_OK;
 }
 
@@ -747,7 +805,8 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
     return EP_ERR_INVALID_ARG;
   rc = check_device();
   if (rc != EP_OK) return rc;
-  const int tok_blocks = (N + kWaves - 1) / kWaves;
+  const int tok_per_block = p->use_fp8 ? kWaves : kThreads / EP_DISPATCH_TPT;
+  const int tok_blocks = (N + tok_per_block - 1) / tok_per_block;
   const int64_t fill_blocks64 = meta ? (recv_capacity + kFillSlots - 1) / kFillSlots : 0;
   if (fill_blocks64 + tok_blocks > INT32_MAX) return EP_ERR_INVALID_ARG;
   const int grid = tok_blocks + (int)fill_blocks64;
@@ -755,7 +814,7 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
   hipStream_t st = (hipStream_t)stream;
   const int H = p->hidden;
   if (!p->use_fp8) {
-    const int q = (H / 8 + 63) / 64;
+    const int q = (H / 8 + EP_DISPATCH_TPT - 1) / EP_DISPATCH_TPT;
     EP_LOG("dispatch bf16 N=%d H=%d K=%d cap=%lld: token blocks=%d fill blocks=%lld nv=%d", N, H,
            p->num_topk, (long long)recv_capacity, tok_blocks, (long long)fill_blocks64, q);
 #define EP_D16(NV)                                                                          \
@@ -765,6 +824,7 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
     if (q <= 1) EP_D16(1);
     else if (q <= 2) EP_D16(2);
     else if (q <= 4) EP_D16(4);
+    else if (q <= 7) EP_D16(7);
     else if (q <= 8) EP_D16(8);
     else if (q <= 14) EP_D16(14);
     else EP_D16(16);
@@ -799,10 +859,11 @@ int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slo
   rc = check_device();
   if (rc != EP_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  const int blocks = (N + kWaves - 1) / kWaves;
-  EP_LOG("combine N=%d H=%d K=%d cap=%lld: blocks=%d nv=%d", N, p->hidden, p->num_topk,
-         (long long)recv_capacity, blocks, EP_COMBINE_NV);
-  combine_kernel<EP_COMBINE_NV><<<blocks, kThreads, 0, st>>>(
+  constexpr int tok_per_block = kThreads / EP_COMBINE_TPT;
+  const int blocks = (N + tok_per_block - 1) / tok_per_block;
+  EP_LOG("combine N=%d H=%d K=%d cap=%lld: blocks=%d tpt=%d nv=%d", N, p->hidden, p->num_topk,
+         (long long)recv_capacity, blocks, EP_COMBINE_TPT, EP_COMBINE_NV);
+  combine_kernel<EP_COMBINE_TPT, EP_COMBINE_NV><<<blocks, kThreads, 0, st>>>(
       (const u32x4*)expert_out, slot_of, topk_weights, (u32x4*)y, N, p->num_topk, p->hidden / 8,
       recv_capacity);
   return check_launch("combine");
