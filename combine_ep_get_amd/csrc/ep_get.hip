@@ -41,17 +41,17 @@
 
 #include "ep_get.h"
 
-#ifndef EP_NT_LOAD
-#define EP_NT_LOAD 1
+// Cache policy of the streaming accesses (measured on MI355X): token rows
+// read by dispatch use ordinary loads, expert rows read by combine use
+// non-temporal loads, and all payload stores are non-temporal.
+#ifndef EP_DISPATCH_NT_LOAD
+#define EP_DISPATCH_NT_LOAD 0
+#endif
+#ifndef EP_COMBINE_NT_LOAD
+#define EP_COMBINE_NT_LOAD 1
 #endif
 #ifndef EP_NT_STORE
 #define EP_NT_STORE 1
-#endif
-#ifndef EP_COMBINE_NV
-#define EP_COMBINE_NV 2
-#endif
-#ifndef EP_COMBINE_TPT
-#define EP_COMBINE_TPT 64
 #endif
 #ifndef EP_DISPATCH_TPT
 #define EP_DISPATCH_TPT 64
@@ -59,20 +59,23 @@
 
 namespace {
 
-constexpr int kThreads = 256;             // 4 wavefronts per block
+#ifndef EP_BLOCK
+#define EP_BLOCK 256
+#endif
+#ifndef EP_DISPATCH_KINNER
+#define EP_DISPATCH_KINNER 0
+#endif
+constexpr int kThreads = EP_BLOCK;        // threads per block of the row kernels
 constexpr int kWaves = kThreads / 64;
 constexpr int kFillPerThread = 8;         // padding-fill: slots per thread
-constexpr int kFillSlots = kThreads * kFillPerThread;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- memory ops
+template <bool NT>
 __device__ __forceinline__ u32x4 ld16(const u32x4* p) {
-#if EP_NT_LOAD
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
 }
 
 __device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
@@ -97,16 +100,6 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 // bf16 halves of a 32-bit word -> float32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// float32 -> bf16 bits, round to nearest even (adding 0x7FFF plus the lowest
-// kept bit carries exactly when the dropped half is above 1/2, or equal to
-// 1/2 with an odd kept part).  NaN stays a quiet NaN with its sign.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 
 // float32 -> OCP E4M3FN code, round to nearest even, saturating at +-448.
 //  |y| >= 448     : largest finite code 0x7E (also +-inf)
@@ -190,23 +183,25 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(
   if (tid == 0) blk_err[b] = err;
 }
 
-// Phase 2: scan and stable slots.  Every block first rebuilds, from the
-// per-block histograms of phase 1, what it needs of the device-wide scan:
-// its own exclusive prefix over earlier blocks for each expert and the
-// per-expert totals, whose padded exclusive scan gives the region offsets
-// (redundant per block, but all loads are independent and in flight together,
-// which is cheaper than a serial single-block scan plus another launch).
-// Block 0 publishes the offsets, receive counts and error word; the first
-// block of each source publishes that source's rows of the count matrices.
+// Phase 2: scan and stable slots, 1024 threads per block.  Every block first
+// rebuilds, from the per-block histograms of phase 1, what it needs of the
+// device-wide scan: its own exclusive prefix over earlier blocks for each
+// expert and the per-expert totals, whose padded exclusive scan gives the
+// region offsets.  This is redundant per block, but the histogram reads are
+// split over 1024/E slices of blocks so that they are all in flight at once,
+// which is cheaper than a serial scan in a separate launch.  Block 0
+// publishes the offsets, receive counts and error word; the first block of
+// each source publishes that source's rows of the count matrices.
 //
-// Slots: pairs are taken in (token, k) order, 256 per round; within a
+// Slots: pairs are taken in (token, k) order, 1024 per round; within a
 // wavefront each lane ORs its bit into the 64-bit LDS mask of its expert, so
 // the rank among equal experts is the popcount of the lower lanes' bits, plus
 // the counts of lower wavefronts, plus everything the block and the earlier
 // blocks already placed for that expert.
-constexpr int kEPerThread = EP_MAX_EXPERTS / kThreads;  // experts per thread in the scan
+constexpr int kAssignThreads = 1024;
+constexpr int kAssignWaves = kAssignThreads / 64;
 
-__global__ __launch_bounds__(kThreads) void layout_assign_kernel(
+__global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_cnt,
     const int32_t* __restrict__ blk_rank, const int32_t* __restrict__ blk_err,
     int32_t* __restrict__ err_word, int32_t* __restrict__ num_tokens_per_rank,
@@ -214,8 +209,9 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     int32_t* __restrict__ off, int32_t* __restrict__ slot_of, int K, int E, int R, int T,
     int CB, int C, int B, int A) {
   __shared__ int base[EP_MAX_EXPERTS];
-  __shared__ int wsum[kWaves];
-  __shared__ unsigned long long masks[kWaves][EP_MAX_EXPERTS];
+  __shared__ int part_tot[kAssignThreads], part_pre[kAssignThreads], part_src[kAssignThreads];
+  __shared__ int wsum[kAssignWaves];
+  extern __shared__ unsigned long long masks[];  // [kAssignWaves][E]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x, src = b / CB, c = b % CB;
   const int t0 = src * T + c * C;
@@ -224,57 +220,51 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
   const int np = (t1 - t0) * K;
   const int e_first = (tid < np) ? topk_idx[p0 + tid] : -1;  // round 0, loaded early
 
-  // (a) per-expert prefix over blocks < b, totals, and this source's row
-  int pre[kEPerThread], tot[kEPerThread], srow[kEPerThread];
-#pragma unroll
-  for (int j = 0; j < kEPerThread; j++) {
-    pre[j] = 0;
-    tot[j] = 0;
-    srow[j] = 0;
-  }
+  // (a) slice sl of the blocks for expert e: prefix (< b), total, this source
+  const int S = kAssignThreads / E;
   const int s0 = src * CB, s1 = s0 + CB;
+  {
+    const int e = tid % E, sl = tid / E;
+    if (sl < S) {
+      const int bb0 = (int)((int64_t)B * sl / S), bb1 = (int)((int64_t)B * (sl + 1) / S);
+      int tot = 0, pre = 0, srow = 0;
+      int bb = bb0;
+      for (; bb + 16 <= bb1; bb += 16) {
+        int v[16];
 #pragma unroll
-  for (int j = 0; j < kEPerThread; j++) {
-    const int e = tid + j * kThreads;
-    if (e >= E) break;
-    int bb = 0;
-    for (; bb + 16 <= B; bb += 16) {
-      int v[16];
+        for (int u = 0; u < 16; u++) v[u] = blk_cnt[(int64_t)(bb + u) * E + e];
 #pragma unroll
-      for (int u = 0; u < 16; u++) v[u] = blk_cnt[(int64_t)(bb + u) * E + e];
-#pragma unroll
-      for (int u = 0; u < 16; u++) {
-        const int bi = bb + u;
-        tot[j] += v[u];
-        if (bi < b) pre[j] += v[u];
-        if (bi >= s0 && bi < s1) srow[j] += v[u];
+        for (int u = 0; u < 16; u++) {
+          const int bi = bb + u;
+          tot += v[u];
+          if (bi < b) pre += v[u];
+          if (bi >= s0 && bi < s1) srow += v[u];
+        }
       }
+      for (; bb < bb1; bb++) {
+        const int v = blk_cnt[(int64_t)bb * E + e];
+        tot += v;
+        if (bb < b) pre += v;
+        if (bb >= s0 && bb < s1) srow += v;
+      }
+      part_tot[sl * E + e] = tot;
+      part_pre[sl * E + e] = pre;
+      part_src[sl * E + e] = srow;
     }
-    for (; bb < B; bb++) {
-      const int v = blk_cnt[(int64_t)bb * E + e];
-      tot[j] += v;
-      if (bb < b) pre[j] += v;
-      if (bb >= s0 && bb < s1) srow[j] += v;
-    }
-  }
-  // (b) padded exclusive scan over experts: thread tid owns experts
-  //     tid, tid+256, ...; scan in expert order via LDS
-#pragma unroll
-  for (int j = 0; j < kEPerThread; j++) {
-    const int e = tid + j * kThreads;
-    if (e < E) base[e] = (tot[j] + A - 1) / A * A;
   }
   __syncthreads();
-  // each thread sums a run of kEPerThread consecutive experts, then a block scan
-  int run[kEPerThread];
-  int acc = 0;
-#pragma unroll
-  for (int j = 0; j < kEPerThread; j++) {
-    const int e = tid * kEPerThread + j;
-    run[j] = (e < E) ? base[e] : 0;
-    acc += run[j];
+  // (b) thread tid < E owns expert tid: reduce the slices, then a padded
+  //     exclusive scan over experts across the whole block
+  int tot = 0, pre = 0, srow = 0;
+  if (tid < E) {
+    for (int sl = 0; sl < S; sl++) {
+      tot += part_tot[sl * E + tid];
+      pre += part_pre[sl * E + tid];
+      srow += part_src[sl * E + tid];
+    }
   }
-  int x = acc;
+  const int padded = (tid < E) ? (tot + A - 1) / A * A : 0;
+  int x = padded;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int y = __shfl_up(x, d);
@@ -284,32 +274,22 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
   __syncthreads();
   int wpre = 0;
   for (int ww = 0; ww < w; ww++) wpre += wsum[ww];
-  int excl = wpre + x - acc;  // exclusive prefix of this thread's run
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kEPerThread; j++) {
-    const int e = tid * kEPerThread + j;
-    if (e < E) base[e] = excl;  // base[e] now holds off[e]
-    excl += run[j];
-  }
-  if (b == 0 && tid == kThreads - 1) off[E] = excl;
-  __syncthreads();
-  // (c) publish, then turn base[] into this block's first slot per expert
-#pragma unroll
-  for (int j = 0; j < kEPerThread; j++) {
-    const int e = tid + j * kThreads;
-    if (e >= E) break;
+  const int incl = wpre + x;
+  // (c) publish, and set base[] to this block's first slot per expert
+  if (tid < E) {
+    const int offe = incl - padded;
     if (b == 0) {
-      off[e] = base[e];
-      num_recv[e] = tot[j];
+      off[tid] = offe;
+      num_recv[tid] = tot;
+      if (tid == E - 1) off[E] = incl;
     }
-    if (c == 0) num_tokens_per_expert[(int64_t)src * E + e] = srow[j];
-    base[e] += pre[j];
+    if (c == 0) num_tokens_per_expert[(int64_t)src * E + tid] = srow;
+    base[tid] = offe + pre;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ww++) masks[ww][e] = 0ull;
+    for (int ww = 0; ww < kAssignWaves; ww++) masks[ww * E + tid] = 0ull;
   }
   if (c == 0) {
-    for (int r = tid; r < R; r += kThreads) {
+    for (int r = tid; r < R; r += kAssignThreads) {
       int v = 0;
       for (int bb = s0; bb < s1; bb++) v += blk_rank[(int64_t)bb * R + r];
       num_tokens_per_rank[(int64_t)src * R + r] = v;
@@ -317,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
   }
   if (b == 0) {
     int ev = 0;
-    for (int bb = tid; bb < B; bb += kThreads) ev |= blk_err[bb];
+    for (int bb = tid; bb < B; bb += kAssignThreads) ev |= blk_err[bb];
     ev = __syncthreads_or(ev);
     if (tid == 0) *err_word = ev ? EP_LAYOUT_ERR_INDEX : 0;
   }
@@ -325,25 +305,25 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
 
   // (d) stable ranks
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int r0 = 0; r0 < np; r0 += kThreads) {
+  for (int r0 = 0; r0 < np; r0 += kAssignThreads) {
     const int p = r0 + tid;
     int e = e_first;
     if (r0 > 0) e = (p < np) ? topk_idx[p0 + p] : -1;
     const bool ok = (e >= 0 && e < E);
-    if (ok) atomicOr(&masks[w][e], 1ull << lane);
+    if (ok) atomicOr(&masks[w * E + e], 1ull << lane);
     __syncthreads();
     int slot = -1;
     unsigned long long m = 0;
     if (ok) {
-      m = masks[w][e];
+      m = masks[w * E + e];
       int pw = 0;
-      for (int w2 = 0; w2 < w; w2++) pw += __popcll(masks[w2][e]);
+      for (int w2 = 0; w2 < w; w2++) pw += __popcll(masks[w2 * E + e]);
       slot = base[e] + pw + __popcll(m & below);
     }
     __syncthreads();
     if (ok && (m & below) == 0ull) {  // lowest lane of this expert in this wave
       atomicAdd(&base[e], __popcll(m));
-      masks[w][e] = 0ull;
+      masks[w * E + e] = 0ull;
     }
     __syncthreads();
     if (p < np) slot_of[p0 + p] = slot;
@@ -369,12 +349,13 @@ __global__ __launch_bounds__(kThreads) void layout_empty_kernel(
 // Padding / unused slots of [0, cap): source -1, weight 0.  A slot s below
 // off[E] belongs to the expert e with off[e] <= s < off[e+1] (binary search
 // over the offsets staged in LDS) and is padding iff s - off[e] >= count[e].
+template <int BLK>
 __device__ __forceinline__ void fill_padding(int fb, const int32_t* __restrict__ off,
                                              const int32_t* __restrict__ recv_cnt, int E,
                                              int64_t cap, int32_t* __restrict__ recv_src,
                                              float* __restrict__ recv_w, int* s_off, int* s_cnt) {
   const int tid = threadIdx.x;
-  for (int e = tid; e <= E; e += kThreads) {
+  for (int e = tid; e <= E; e += BLK) {
     s_off[e] = off[e];
     if (e < E) s_cnt[e] = recv_cnt[e];
   }
@@ -382,7 +363,7 @@ __device__ __forceinline__ void fill_padding(int fb, const int32_t* __restrict__
   const int used = s_off[E];
 #pragma unroll
   for (int j = 0; j < kFillPerThread; j++) {
-    const int64_t s = (int64_t)fb * kFillSlots + (int64_t)j * kThreads + tid;
+    const int64_t s = (int64_t)fb * BLK * kFillPerThread + (int64_t)j * BLK + tid;
     if (s >= cap) break;
     bool pad = true;
     if (s < used) {
@@ -424,8 +405,8 @@ __device__ __forceinline__ void write_meta(int t, int K, int lane, int myslot,
 // bf16 rows: TPT threads (a multiple of 64) per token; NV 16-byte chunks per
 // thread per pass, so one pass moves TPT*NV*16 bytes of the row, which is read
 // once into VGPRs and then stored to each of the token's K slots.
-template <int TPT, int NV>
-__global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
+template <int TPT, int NV, int BLK>
+__global__ __launch_bounds__(BLK) void dispatch_bf16_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
     const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
     u32x4* __restrict__ recv_x, int32_t* __restrict__ recv_src, float* __restrict__ recv_w,
@@ -433,10 +414,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
   __shared__ int s_off[EP_MAX_EXPERTS + 1];
   __shared__ int s_cnt[EP_MAX_EXPERTS];
   if ((int)blockIdx.x >= tok_blocks) {
-    fill_padding(blockIdx.x - tok_blocks, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
+    fill_padding<BLK>(blockIdx.x - tok_blocks, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
     return;
   }
-  constexpr int kTok = kThreads / TPT;
+  constexpr int kTok = BLK / TPT;
   const int t = uniform(blockIdx.x * kTok + (int)(threadIdx.x / TPT));
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
@@ -448,8 +429,19 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < NV; i++) {
       const int c = base + i * TPT + vl;
-      if (c < H8) v[i] = ld16(row + c);
+      if (c < H8) v[i] = ld16<EP_DISPATCH_NT_LOAD>(row + c);
     }
+#if EP_DISPATCH_KINNER
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int c = base + i * TPT + vl;
+      for (int k = 0; k < K; k++) {
+        const int s = lane_value(myslot, k);
+        if (s < 0) continue;
+        if (c < H8) st16(recv_x + (int64_t)s * H8 + c, v[i]);
+      }
+    }
+#else
     for (int k = 0; k < K; k++) {
       const int s = lane_value(myslot, k);
       if (s < 0) continue;
@@ -460,6 +452,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
         if (c < H8) st16(dst + c, v[i]);
       }
     }
+#endif
   }
   if (vl < 64) write_meta(t, K, lane, myslot, w, recv_src, recv_w);
 }
@@ -478,7 +471,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
   __shared__ int s_off[EP_MAX_EXPERTS + 1];
   __shared__ int s_cnt[EP_MAX_EXPERTS];
   if ((int)blockIdx.x >= tok_blocks) {
-    fill_padding(blockIdx.x - tok_blocks, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
+    fill_padding<kThreads>(blockIdx.x - tok_blocks, off, recv_cnt, E, cap, recv_src, recv_w,
+                           s_off, s_cnt);
     return;
   }
   const int t = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
@@ -493,8 +487,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     for (int i = 0; i < NI; i++) {
       const int ch = pbase + i * 1024 + lane * 16;
       if (ch < H) {
-        v[i][0] = ld16(row + (ch >> 3));
-        v[i][1] = ld16(row + (ch >> 3) + 1);
+        v[i][0] = ld16<EP_DISPATCH_NT_LOAD>(row + (ch >> 3));
+        v[i][1] = ld16<EP_DISPATCH_NT_LOAD>(row + (ch >> 3) + 1);
       }
     }
     float my_scale = 0.0f;
@@ -554,15 +548,97 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
 }
 
 // ---------------------------------------------------------------- combine
-// TPT threads (a multiple of 64) per token.  For each pass of NV 16-byte
-// chunks per thread, the rows of up to 8 pairs are loaded first (all in
-// flight), then accumulated in ascending k: acc = acc + w_k * row_k
-// (separately rounded multiply and add), and stored as bf16 (RNE).
+// Combine: TPT threads (a multiple of 64) per token, one 16-byte chunk per
+// thread per pass.  The rows of the token's pairs are loaded, then
+// accumulated in ascending k: acc = acc + w_k * row_k (separately rounded
+// multiply and add, matching the contract bit for bit), and stored as bf16
+// with round-to-nearest-even (v_cvt_pk_bf16_f32).
+//
+// The launch picks TPT so that a row is covered in one pass whenever it fits
+// in 16 wavefronts (896 threads at hidden 7168): every expert row of the token
+// is then requested as a whole, at once.  Measured on MI355X this matters far
+// more than arithmetic, which the memory time hides completely: one wavefront
+// walking 1 KiB pieces of the K rows reaches ~5.2 TB/s, whole rows ~5.8 TB/s.
+// Wider rows take several passes, software-pipelined for K <= 8 (pass i+1's
+// loads in flight while pass i is accumulated).  Loads are branch-free (the
+// column index is clamped and invalid slots read row 0); only the
+// accumulation skips slots that hold no pair.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 template <int TPT, int NV>
-__global__ __launch_bounds__(kThreads) void combine_kernel(
+__device__ __forceinline__ void combine_load8(u32x4 (&v)[8][NV], const u32x4* __restrict__ eo,
+                                              int myslot, int K, int base, int vl, int H8) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    int s = (j < K) ? lane_value(myslot, j) : -1;
+    s = s < 0 ? 0 : s;
+    const u32x4* r = eo + (int64_t)s * H8;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int c = min(base + i * TPT + vl, H8 - 1);
+      v[j][i] = ld16<EP_COMBINE_NT_LOAD>(r + c);
+    }
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void combine_accum8(float (&acc)[NV][8], const u32x4 (&v)[8][NV],
+                                               int myslot, float myw, int K) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int s = (j < K) ? lane_value(myslot, j) : -1;
+    if (s < 0) continue;
+    const float wk = lane_value(myw, j);
+#pragma unroll
+    for (int i = 0; i < NV; i++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        acc[i][2 * q] = acc[i][2 * q] + wk * bf16_lo(v[j][i][q]);
+        acc[i][2 * q + 1] = acc[i][2 * q + 1] + wk * bf16_hi(v[j][i][q]);
+      }
+  }
+}
+
+template <int TPT, int NV>
+__device__ __forceinline__ void combine_store(const float (&acc)[NV][8], u32x4* __restrict__ yrow,
+                                              int base, int vl, int H8) {
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int c = base + i * TPT + vl;
+    if (c < H8) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; q++) o[q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
+      st16(yrow + c, o);
+    }
+  }
+}
+
+template <int TPT, int NV>
+__device__ __forceinline__ void combine_pass8(const u32x4 (&v)[8][NV], int myslot, float myw,
+                                              int K, u32x4* __restrict__ yrow, int base, int vl,
+                                              int H8) {
+  float acc[NV][8];
+#pragma unroll
+  for (int i = 0; i < NV; i++)
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[i][j] = 0.0f;
+  combine_accum8<NV>(acc, v, myslot, myw, K);
+  combine_store<TPT, NV>(acc, yrow, base, vl, H8);
+}
+
+template <int TPT, int BLK, bool MULTI>
+__global__ __launch_bounds__(BLK) void combine_kernel(
     const u32x4* __restrict__ eo, const int32_t* __restrict__ slot_of,
     const float* __restrict__ w, u32x4* __restrict__ y, int N, int K, int H8, int64_t cap) {
-  constexpr int kTok = kThreads / TPT;
+  constexpr int kTok = BLK / TPT;
+  constexpr int kStep = TPT;  // one 16-byte chunk per thread per pass
   const int t = uniform(blockIdx.x * kTok + (int)(threadIdx.x / TPT));
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
@@ -570,53 +646,35 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   const int myslot = load_slot(slot_of, t, K, lane, cap);
   const float myw = (lane < K) ? w[(int64_t)t * K + lane] : 0.0f;
   u32x4* yrow = y + (int64_t)t * H8;
-  for (int base = 0; base < H8; base += TPT * NV) {
-    float acc[NV][8];
+  if (MULTI && K <= 8) {
+    u32x4 va[8][1], vb[8][1];
+    combine_load8<TPT, 1>(va, eo, myslot, K, 0, vl, H8);
+    for (int base = 0; base < H8; base += 2 * kStep) {
+      const int b1 = base + kStep;
+      if (b1 < H8) combine_load8<TPT, 1>(vb, eo, myslot, K, b1, vl, H8);
+      combine_pass8<TPT, 1>(va, myslot, myw, K, yrow, base, vl, H8);
+      if (b1 >= H8) break;
+      const int b2 = b1 + kStep;
+      if (b2 < H8) combine_load8<TPT, 1>(va, eo, myslot, K, b2, vl, H8);
+      combine_pass8<TPT, 1>(vb, myslot, myw, K, yrow, b1, vl, H8);
+    }
+    return;
+  }
+  // one pass when H8 <= TPT; K > 8 goes through groups of 8 rows, accumulated
+  // group after group so that the order over k is kept
+  for (int base = 0; base < H8; base += kStep) {
+    float acc[1][8];
 #pragma unroll
-    for (int i = 0; i < NV; i++)
-#pragma unroll
-      for (int j = 0; j < 8; j++) acc[i][j] = 0.0f;
+    for (int j = 0; j < 8; j++) acc[0][j] = 0.0f;
     for (int kg = 0; kg < K; kg += 8) {
-      u32x4 v[8][NV];
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int k = kg + j;
-        const int s = (k < K) ? lane_value(myslot, k) : -1;
-        if (s >= 0) {
-          const u32x4* r = eo + (int64_t)s * H8;
-#pragma unroll
-          for (int i = 0; i < NV; i++) {
-            const int c = base + i * TPT + vl;
-            if (c < H8) v[j][i] = ld16(r + c);
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int k = kg + j;
-        const int s = (k < K) ? lane_value(myslot, k) : -1;
-        if (s < 0) continue;
-        const float wk = lane_value(myw, k);
-#pragma unroll
-        for (int i = 0; i < NV; i++)
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            acc[i][2 * q] = acc[i][2 * q] + wk * bf16_lo(v[j][i][q]);
-            acc[i][2 * q + 1] = acc[i][2 * q + 1] + wk * bf16_hi(v[j][i][q]);
-          }
-      }
+      u32x4 v[8][1];
+      const int rem = K - kg;
+      const int slot_g = __shfl_down(myslot, kg);  // lane j now holds pair kg+j
+      const float w_g = __shfl_down(myw, kg);
+      combine_load8<TPT, 1>(v, eo, slot_g, rem, base, vl, H8);
+      combine_accum8<1>(acc, v, slot_g, w_g, rem);
     }
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-      const int c = base + i * TPT + vl;
-      if (c < H8) {
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-          o[q] = bf16_rne(acc[i][2 * q]) | (bf16_rne(acc[i][2 * q + 1]) << 16);
-        st16(yrow + c, o);
-      }
-    }
+    combine_store<TPT, 1>(acc, yrow, base, vl, H8);
   }
 }
 
@@ -717,7 +775,8 @@ void launch_dispatch_bf16(dim3 grid, hipStream_t st, const ep_problem_t* p, cons
                           const float* w, const int32_t* slot_of, const int32_t* off,
                           const int32_t* cnt, void* recv_x, int32_t* recv_src, float* recv_w,
                           int64_t cap, int tok_blocks) {
-  dispatch_bf16_kernel<EP_DISPATCH_TPT, NV><<<grid, kThreads, 0, st>>>(
+  constexpr int blk = EP_DISPATCH_TPT > kThreads ? EP_DISPATCH_TPT : kThreads;
+  dispatch_bf16_kernel<EP_DISPATCH_TPT, NV, blk><<<grid, blk, 0, st>>>(
       (const u32x4*)x, w, slot_of, off, cnt, (u32x4*)recv_x, recv_src, recv_w, p->num_tokens,
       p->num_topk, p->num_experts, p->hidden / 8, cap, tok_blocks);
 }
@@ -730,6 +789,42 @@ void launch_dispatch_fp8(dim3 grid, hipStream_t st, const ep_problem_t* p, const
   dispatch_fp8_kernel<NI><<<grid, kThreads, 0, st>>>(
       (const u32x4*)x, w, slot_of, off, cnt, (u32x4*)recv_x, recv_scales, recv_src, recv_w,
       p->num_tokens, p->num_topk, p->num_experts, p->hidden, cap, tok_blocks);
+}
+
+template <int Q, bool MULTI>
+void launch_combine_q(int N, hipStream_t st, const void* eo, const int32_t* slot_of,
+                      const float* w, void* y, int K, int H8, int64_t cap) {
+  constexpr int TPT = 64 * Q;
+  constexpr int BLK = TPT >= 256 ? TPT : 256;
+  constexpr int tok = BLK / TPT;
+  const int blocks = (N + tok - 1) / tok;
+  combine_kernel<TPT, BLK, MULTI><<<blocks, BLK, 0, st>>>((const u32x4*)eo, slot_of, w,
+                                                          (u32x4*)y, N, K, H8, cap);
+}
+
+void launch_combine(int q, int N, hipStream_t st, const void* eo, const int32_t* slot_of,
+                    const float* w, void* y, int K, int H8, int64_t cap) {
+#define EP_CQ(Q) launch_combine_q<Q, false>(N, st, eo, slot_of, w, y, K, H8, cap)
+  switch (q) {
+    case 1: EP_CQ(1); break;
+    case 2: EP_CQ(2); break;
+    case 3:
+    case 4: EP_CQ(4); break;
+    case 5: EP_CQ(5); break;
+    case 6: EP_CQ(6); break;
+    case 7: EP_CQ(7); break;
+    case 8: EP_CQ(8); break;
+    case 9: EP_CQ(9); break;
+    case 10: EP_CQ(10); break;
+    case 11: EP_CQ(11); break;
+    case 12: EP_CQ(12); break;
+    case 13: EP_CQ(13); break;
+    case 14: EP_CQ(14); break;
+    case 15: EP_CQ(15); break;
+    case 16: EP_CQ(16); break;
+    default: launch_combine_q<16, true>(N, st, eo, slot_of, w, y, K, H8, cap); break;
+  }
+#undef EP_CQ
 }
 
 }  // namespace
@@ -780,7 +875,8 @@ int ep_get_layout(const ep_problem_t* p, const int32_t* topk_idx, int32_t* num_t
   layout_count_kernel<<<pl.B, kThreads, 0, st>>>(topk_idx, is_token_in_rank, blk_cnt, blk_rank,
                                                  blk_err, K, E, R, L, T, pl.CB, pl.C);
   if ((rc = check_launch("layout_count")) != EP_OK) return rc;
-  layout_assign_kernel<<<pl.B, kThreads, 0, st>>>(
+  const size_t mask_bytes = sizeof(unsigned long long) * kAssignWaves * (size_t)E;
+  layout_assign_kernel<<<pl.B, kAssignThreads, mask_bytes, st>>>(
       topk_idx, blk_cnt, blk_rank, blk_err, err, num_tokens_per_rank, num_tokens_per_expert,
       num_recv_per_expert, expert_slot_offset, slot_of, K, E, R, T, pl.CB, pl.C, pl.B,
       p->expert_alignment);
@@ -805,9 +901,11 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
     return EP_ERR_INVALID_ARG;
   rc = check_device();
   if (rc != EP_OK) return rc;
-  const int tok_per_block = p->use_fp8 ? kWaves : kThreads / EP_DISPATCH_TPT;
+  constexpr int dblk = EP_DISPATCH_TPT > kThreads ? EP_DISPATCH_TPT : kThreads;
+  const int tok_per_block = p->use_fp8 ? kWaves : dblk / EP_DISPATCH_TPT;
   const int tok_blocks = (N + tok_per_block - 1) / tok_per_block;
-  const int64_t fill_blocks64 = meta ? (recv_capacity + kFillSlots - 1) / kFillSlots : 0;
+  const int64_t fill_slots = (int64_t)(p->use_fp8 ? kThreads : dblk) * kFillPerThread;
+  const int64_t fill_blocks64 = meta ? (recv_capacity + fill_slots - 1) / fill_slots : 0;
   if (fill_blocks64 + tok_blocks > INT32_MAX) return EP_ERR_INVALID_ARG;
   const int grid = tok_blocks + (int)fill_blocks64;
   if (grid == 0) return EP_OK;
@@ -859,13 +957,11 @@ int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slo
   rc = check_device();
   if (rc != EP_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  constexpr int tok_per_block = kThreads / EP_COMBINE_TPT;
-  const int blocks = (N + tok_per_block - 1) / tok_per_block;
-  EP_LOG("combine N=%d H=%d K=%d cap=%lld: blocks=%d tpt=%d nv=%d", N, p->hidden, p->num_topk,
-         (long long)recv_capacity, blocks, EP_COMBINE_TPT, EP_COMBINE_NV);
-  combine_kernel<EP_COMBINE_TPT, EP_COMBINE_NV><<<blocks, kThreads, 0, st>>>(
-      (const u32x4*)expert_out, slot_of, topk_weights, (u32x4*)y, N, p->num_topk, p->hidden / 8,
-      recv_capacity);
+  const int H8 = p->hidden / 8;
+  const int q = (H8 + 63) / 64;  // wavefronts for one chunk per thread
+  EP_LOG("combine N=%d H=%d K=%d cap=%lld: waves per token=%d%s", N, p->hidden, p->num_topk,
+         (long long)recv_capacity, q > 16 ? 16 : (q == 3 ? 4 : q), q > 16 ? " (multi-pass)" : "");
+  launch_combine(q, N, st, expert_out, slot_of, topk_weights, y, p->num_topk, H8, recv_capacity);
   return check_launch("combine");
 }
 

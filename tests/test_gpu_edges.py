@@ -169,3 +169,51 @@ def test_fp8_quantiser_exhaustive_on_device():
     idx = np.arange(ntok, dtype=np.int32).reshape(ntok, 1) % 16
     say(f"quantiser exhaustive: {ng} groups in {ntok} tokens")
     run_case(idx, H=G * 128, E=16, R=4, A=1, fp8=True, x_bits=x_bits)
+
+
+def test_combine_bf16_rounding_at_ties_on_device():
+    """The bf16 store of combine rounds to nearest even: for every normal bf16
+    value a (exponent field 9..246, both signs) the second pair adds b = half
+    an ulp of a (an exact tie), a little more, or a little less, with either
+    sign; a + b is exact in fp32, so the stored bf16 is decided by the
+    rounding rule alone.  Compared bit for bit with the oracle."""
+    allv = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ex = (allv >> 7) & 0xFF
+    a = allv[(ex >= 9) & (ex <= 246)]
+    ea = ((a >> 7) & 0xFF).astype(np.int64)
+    sign = (a & 0x8000).astype(np.uint16)
+
+    def bf16_pow2(e):                      # bf16 bits of 2^(e - 127)
+        return (e << 7).astype(np.uint16)
+
+    half = bf16_pow2(ea - 8)                               # exact tie
+    above = (bf16_pow2(ea - 8) | 0x01).astype(np.uint16)   # 2^(e-8) (1 + 2^-7)
+    below = (bf16_pow2(ea - 9) | 0x7F).astype(np.uint16)   # 2^(e-8) - 2^(e-16)
+    pairs_a, pairs_b = [], []
+    for bb in (half, above, below):
+        for same in (True, False):
+            pairs_a.append(a)
+            pairs_b.append(bb | (sign if same else (sign ^ 0x8000)))
+    va = np.concatenate(pairs_a)
+    vb = np.concatenate(pairs_b)
+    H, R, E = 1024, 4, 8
+    n = -(-va.size // H)
+    n = -(-n // R) * R
+    A_rows = np.zeros(n * H, np.uint16)
+    B_rows = np.zeros(n * H, np.uint16)
+    A_rows[:va.size] = va
+    B_rows[:vb.size] = vb
+    idx = np.stack([np.arange(n) % E, (np.arange(n) + 1) % E], axis=1).astype(np.int32)
+    ref = oracle.layout(idx, E, R, 1)
+    cap = ep.recv_capacity(n, 2, E, R, 1)
+    eo = np.zeros((cap, H), np.uint16)
+    eo[ref["slot_of"][:, 0]] = A_rows.reshape(n, H)
+    eo[ref["slot_of"][:, 1]] = B_rows.reshape(n, H)
+    wts = np.ones((n, 2), np.float32)
+    say(f"bf16 rounding: {va.size} tie / near-tie sums in {n} tokens")
+    lay = ep.get_layout(torch.from_numpy(idx).cuda(), E, R, 1)
+    y = ep.combine(dev_bf16(eo), lay, torch.from_numpy(wts).cuda())
+    torch.cuda.synchronize()
+    ref_y, _ = oracle.combine(eo, ref["slot_of"], wts)
+    got = host_u16(y)
+    np.testing.assert_array_equal(got, ref_y)
