@@ -118,6 +118,80 @@ def ceilings(nbytes=1 << 30):
     return res
 
 
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(args):
+    """Write the profiles/ summaries from three rocprofv3 output directories:
+    --kernel-trace --stats (trace), --pmc FETCH_SIZE (fetch), --pmc WRITE_SIZE
+    (write), all taken on `bench.py --config <id>`.  Counter values are KiB per
+    dispatch; each is scaled by what the same counter reads for the benchmark's
+    1 GiB plain copy kernel (ceiling measurement) in the same run."""
+    from combine_ep_get_amd import workloads as wl
+    w = wl.CONFIGS[args.config]
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    cmd_base = f"python3 bench.py --config {args.config}"
+    # kernel trace statistics
+    stats = _csv_rows(os.path.join(args.trace_dir, "run_kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel statistics: {w.desc}",
+             f"# command: cd /tmp && rocprofv3 --kernel-trace --stats -T -f csv -d <out> -o run -- "
+             f"{cmd_base} --steps 20 --warmup 5 --cpu-seconds 0 --no-ceiling",
+             f"# kernel source sha256: {source_sha()}",
+             f"{'kernel':28s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for r in stats:
+        lines.append(f"{r['Name'][:28]:28s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                     f"{float(r['Percentage']):6.2f}")
+    step_us = sum(float(r["AverageNs"]) for r in stats
+                  if r["Name"].startswith(("layout_", "dispatch_", "combine_"))) / 1e3
+    lines.append(f"sum of per-step kernel averages: {step_us:.2f} us")
+    open(os.path.join(out_dir, f"kernel_trace_{w.name}.txt"), "w").write("\n".join(lines) + "\n")
+
+    def per_kernel(path):
+        acc = {}
+        for r in _csv_rows(path):
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch = per_kernel(os.path.join(args.fetch_dir, "run_counter_collection.csv"))
+    write = per_kernel(os.path.join(args.write_dir, "run_counter_collection.csv"))
+    copy_kib = (1 << 30) / 1024.0
+    f_scale = copy_kib / fetch["copy_kernel"]
+    w_scale = copy_kib / write["copy_kernel"]
+    disp_b, comb_b = algorithmic_bytes(w)
+    dk = "dispatch_fp8_kernel" if w.fp8 else "dispatch_bf16_kernel"
+    for short, kname, alg in (("dispatch_fp8" if w.fp8 else "dispatch_bf16", dk, disp_b),
+                              ("combine", "combine_kernel", comb_b)):
+        fb = fetch[kname] * f_scale * 1024
+        wb = write[kname] * w_scale * 1024
+        txt = [f"# HBM byte audit (rocprofv3 --pmc), {kname}, {w.desc}",
+               f"# commands: cd /tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv -d <out> -o run -- "
+               f"{cmd_base} --steps 3 --warmup 1 --cpu-seconds 0",
+               f"#           cd /tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv -d <out> -o run -- "
+               f"{cmd_base} --steps 3 --warmup 1 --cpu-seconds 0",
+               "# scale: counter KiB of the 1 GiB copy kernel in the same run -> bytes",
+               f"kernel: {kname}",
+               f"workload: {w.name}",
+               f"source_sha256: {source_sha()}",
+               f"fetch_kib_per_dispatch: {fetch[kname]:.1f}",
+               f"write_kib_per_dispatch: {write[kname]:.1f}",
+               f"copy_kernel_fetch_kib: {fetch['copy_kernel']:.1f}",
+               f"copy_kernel_write_kib: {write['copy_kernel']:.1f}",
+               f"fetch_scale: {f_scale:.5f}",
+               f"write_scale: {w_scale:.5f}",
+               f"fetch_bytes_per_launch: {fb:.0f}",
+               f"write_bytes_per_launch: {wb:.0f}",
+               f"traffic_bytes_per_launch: {fb + wb:.0f}",
+               f"algorithmic_bytes_per_launch: {alg}",
+               f"traffic_over_algorithmic: {(fb + wb) / alg:.4f}"]
+        open(os.path.join(out_dir, f"traffic_{short}_{w.name}.txt"), "w").write("\n".join(txt) + "\n")
+    print(f"wrote profiles for {w.name}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,7 +202,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget; 0 skips it")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--summarize", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 output dirs and exit")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (virtual EP ranks inside one GPU's "
@@ -184,25 +266,32 @@ def main():
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
     gpu_step_ms = g0.elapsed_time(g1) / args.steps
-    # Per-kernel durations: the same steps again, with an event between kernels
-    # (each event record costs a few microseconds of queue time, so these steps
-    # are not the ones the headline number comes from).
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    lay_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    dis_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-    com_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    # Per-kernel durations: each kernel launched `steps` times back to back
+    # between two events on the stream the library launches on (the inputs of
+    # every launch are the ones the timed steps used).
+    def per_launch_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    lay_ms = per_launch_ms(lambda: ep.get_layout(idx, w.E, w.R, w.A, out=lay))
+    dis_ms = per_launch_ms(lambda: ep.dispatch(x, wts, lay, w.fp8, out=recv))
+    com_ms = per_launch_ms(lambda: ep.combine(eo, lay, wts, out=y))
 
     disp_b, comb_b = algorithmic_bytes(w)
     total_b = disp_b + comb_b
     gbs = total_b / step_s / 1e9
-    if dis_ms.mean() >= com_ms.mean():
-        dom, dom_b, dom_ms = "dispatch", disp_b, dis_ms.mean()
+    if dis_ms >= com_ms:
+        dom_b, dom_ms = disp_b, dis_ms
         dom_kernel = "dispatch_fp8" if w.fp8 else "dispatch_bf16"
     else:
-        dom, dom_b, dom_ms = "combine", comb_b, com_ms.mean()
+        dom_b, dom_ms = comb_b, com_ms
         dom_kernel = "combine"
     achieved = dom_b / (dom_ms * 1e-3) / 1e9
     traffic = read_traffic(dom_kernel, w.name)
@@ -230,13 +319,10 @@ def main():
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": total_b,
         "gpu_ms_per_step": round(gpu_step_ms, 4),
-        "kernel_ms": {"layout": round(float(lay_ms.mean()), 4),
-                      "dispatch": round(float(dis_ms.mean()), 4),
-                      "combine": round(float(com_ms.mean()), 4),
-                      "dispatch_p10": round(float(np.percentile(dis_ms, 10)), 4),
-                      "dispatch_p90": round(float(np.percentile(dis_ms, 90)), 4),
-                      "combine_p10": round(float(np.percentile(com_ms, 10)), 4),
-                      "combine_p90": round(float(np.percentile(com_ms, 90)), 4)},
+        "kernel_ms": {"layout": round(lay_ms, 4), "dispatch": round(dis_ms, 4),
+                      "combine": round(com_ms, 4)},
+        "kernel_gbs": {"dispatch": round(disp_b / (dis_ms * 1e-3) / 1e9, 1),
+                       "combine": round(comb_b / (com_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},

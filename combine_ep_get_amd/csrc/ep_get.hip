@@ -138,48 +138,86 @@ struct Plan {
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
+// Both layout phases stage the block's routing indices in LDS, a tile of
+// whole tokens at a time, issuing every global load of the tile before any of
+// them is used: these kernels are latency-bound, and a chain of dependent
+// global round trips is what would make them slow.
+constexpr int kCountTile = 8192;        // pairs staged per tile in phase 1 (32 KiB of LDS)
+constexpr int kAssignTile = 4096;       // pairs staged per tile in phase 2 (16 KiB of LDS)
+constexpr int kCountThreads = 512;
+constexpr int kFlagBytes = 16384;       // LDS for is_token_in_rank staging
+
+// stage n <= TILE consecutive pairs of topk_idx into sidx[0, n)
+template <int BLK, int TILE>
+__device__ __forceinline__ void stage_idx(int* __restrict__ sidx, const int32_t* __restrict__ idx,
+                                          int n) {
+  constexpr int kPer = TILE / BLK;
+  int v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int q = j * BLK + (int)threadIdx.x;
+    v[j] = (q < n) ? idx[q] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int q = j * BLK + (int)threadIdx.x;
+    if (q < n) sidx[q] = v[j];
+  }
+}
+
 // Phase 1: per-block expert histogram, is_token_in_rank rows and per-block
 // per-rank token counts.  LDS atomics only count (order does not matter).
-__global__ __launch_bounds__(kThreads) void layout_count_kernel(
+__global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     const int32_t* __restrict__ topk_idx, uint8_t* __restrict__ in_rank,
     int32_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_rank, int32_t* __restrict__ blk_err,
     int K, int E, int R, int L, int T, int CB, int C) {
+  __shared__ int sidx[kCountTile];
   __shared__ int hist[EP_MAX_EXPERTS];
   __shared__ int rcnt[EP_MAX_RANKS];
-  __shared__ uint8_t flags[64 * EP_MAX_RANKS];
+  __shared__ uint8_t flags[kFlagBytes];
   __shared__ int err;
+  constexpr int BLK = kCountThreads;
   const int tid = threadIdx.x;
   const int b = blockIdx.x, src = b / CB, c = b % CB;
   const int t0 = src * T + c * C;
   const int t1 = src * T + min((c + 1) * C, T);
-  for (int e = tid; e < E; e += kThreads) hist[e] = 0;
-  for (int r = tid; r < R; r += kThreads) rcnt[r] = 0;
+  const int tok_tile = kCountTile / K;          // whole tokens per tile
+  const int tok_sub = kFlagBytes / R;           // tokens per flag pass (>= 64)
+  for (int e = tid; e < E; e += BLK) hist[e] = 0;
+  for (int r = tid; r < R; r += BLK) rcnt[r] = 0;
   if (tid == 0) err = 0;
-  for (int sub = t0; sub < t1; sub += 64) {
-    const int nt = min(64, t1 - sub);
-    for (int q = tid; q < nt * R; q += kThreads) flags[q] = 0;
+  for (int tt = t0; tt < t1; tt += tok_tile) {
+    const int ntok = min(tok_tile, t1 - tt);
+    const int n = ntok * K;
+    __syncthreads();  // previous tile fully consumed; counters initialised
+    stage_idx<BLK, kCountTile>(sidx, topk_idx + (int64_t)tt * K, n);
     __syncthreads();
-    const int32_t* idx = topk_idx + (int64_t)sub * K;
-    for (int q = tid; q < nt * K; q += kThreads) {
-      int e = idx[q];
-      if (e >= 0 && e < E) {
-        atomicAdd(&hist[e], 1);
-        flags[(q / K) * R + e / L] = 1;
-      } else if (e != -1) {
-        err = EP_LAYOUT_ERR_INDEX;
+    for (int q = tid; q < n; q += BLK) {
+      const int e = sidx[q];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+      else if (e != -1) err = EP_LAYOUT_ERR_INDEX;
+    }
+    for (int sub = 0; sub < ntok; sub += tok_sub) {
+      const int nt = min(tok_sub, ntok - sub);
+      for (int q = tid; q < nt * R; q += BLK) flags[q] = 0;
+      __syncthreads();
+      for (int q = tid; q < nt * K; q += BLK) {
+        const int e = sidx[sub * K + q];
+        if (e >= 0 && e < E) flags[(q / K) * R + e / L] = 1;
       }
+      __syncthreads();
+      uint8_t* out = in_rank + (int64_t)(tt + sub) * R;
+      for (int q = tid; q < nt * R; q += BLK) {
+        const uint8_t v = flags[q];
+        out[q] = v;
+        if (v) atomicAdd(&rcnt[q % R], 1);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    uint8_t* out = in_rank + (int64_t)sub * R;
-    for (int q = tid; q < nt * R; q += kThreads) {
-      uint8_t v = flags[q];
-      out[q] = v;
-      if (v) atomicAdd(&rcnt[q % R], 1);
-    }
-    __syncthreads();
   }
-  for (int e = tid; e < E; e += kThreads) blk_cnt[(int64_t)b * E + e] = hist[e];
-  for (int r = tid; r < R; r += kThreads) blk_rank[(int64_t)b * R + r] = rcnt[r];
+  __syncthreads();
+  for (int e = tid; e < E; e += BLK) blk_cnt[(int64_t)b * E + e] = hist[e];
+  for (int r = tid; r < R; r += BLK) blk_rank[(int64_t)b * R + r] = rcnt[r];
   if (tid == 0) blk_err[b] = err;
 }
 
@@ -188,7 +226,8 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(
 // device-wide scan: its own exclusive prefix over earlier blocks for each
 // expert and the per-expert totals, whose padded exclusive scan gives the
 // region offsets.  This is redundant per block, but the histogram reads are
-// split over 1024/E slices of blocks so that they are all in flight at once,
+// split over 1024/E slices of blocks so that they are all in flight at once
+// (together with the block's routing indices and the per-source rank counts),
 // which is cheaper than a serial scan in a separate launch.  Block 0
 // publishes the offsets, receive counts and error word; the first block of
 // each source publishes that source's rows of the count matrices.
@@ -208,59 +247,74 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_recv,
     int32_t* __restrict__ off, int32_t* __restrict__ slot_of, int K, int E, int R, int T,
     int CB, int C, int B, int A) {
+  constexpr int BLK = kAssignThreads;
+  __shared__ int sidx[kAssignTile];
   __shared__ int base[EP_MAX_EXPERTS];
-  __shared__ int part_tot[kAssignThreads], part_pre[kAssignThreads], part_src[kAssignThreads];
+  __shared__ int rsum[EP_MAX_RANKS];
   __shared__ int wsum[kAssignWaves];
-  extern __shared__ unsigned long long masks[];  // [kAssignWaves][E]
+  // dynamic LDS: the per-wave expert masks [kAssignWaves][E]; its first
+  // 3*BLK ints hold the slice partials of step (a)/(b), which are dead before
+  // the masks are first written in step (c)
+  extern __shared__ unsigned long long masks[];
+  int* part_tot = reinterpret_cast<int*>(masks);
+  int* part_pre = part_tot + BLK;
+  int* part_src = part_pre + BLK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x, src = b / CB, c = b % CB;
   const int t0 = src * T + c * C;
   const int t1 = src * T + min((c + 1) * C, T);
-  const int64_t p0 = (int64_t)t0 * K;
-  const int np = (t1 - t0) * K;
-  const int e_first = (tid < np) ? topk_idx[p0 + tid] : -1;  // round 0, loaded early
-
-  // (a) slice sl of the blocks for expert e: prefix (< b), total, this source
-  const int S = kAssignThreads / E;
+  const int tok_tile = kAssignTile / K;
   const int s0 = src * CB, s1 = s0 + CB;
-  {
-    const int e = tid % E, sl = tid / E;
-    if (sl < S) {
-      const int bb0 = (int)((int64_t)B * sl / S), bb1 = (int)((int64_t)B * (sl + 1) / S);
-      int tot = 0, pre = 0, srow = 0;
-      int bb = bb0;
-      for (; bb + 16 <= bb1; bb += 16) {
-        int v[16];
+
+  // (a) loads: the first tile of routing indices, the per-block histogram
+  //     slices, the per-source rank counts (first block of a source) and the
+  //     error flags (block 0), all issued before anything waits on them
+  const int ntok0 = min(tok_tile, t1 - t0);
+  stage_idx<BLK, kAssignTile>(sidx, topk_idx + (int64_t)t0 * K, ntok0 * K);
+  for (int r = tid; r < R; r += BLK) rsum[r] = 0;
+  const int S = BLK / E;  // slices of the block range per expert
+  const int e_a = tid % E, sl = tid / E;
+  int tot = 0, pre = 0, srow = 0;
+  if (sl < S) {
+    const int bb0 = (int)((int64_t)B * sl / S), bb1 = (int)((int64_t)B * (sl + 1) / S);
+    for (int bb = bb0; bb < bb1; bb += 16) {
+      int v[16];
 #pragma unroll
-        for (int u = 0; u < 16; u++) v[u] = blk_cnt[(int64_t)(bb + u) * E + e];
+      for (int u = 0; u < 16; u++) v[u] = (bb + u < bb1) ? blk_cnt[(int64_t)(bb + u) * E + e_a] : 0;
 #pragma unroll
-        for (int u = 0; u < 16; u++) {
-          const int bi = bb + u;
-          tot += v[u];
-          if (bi < b) pre += v[u];
-          if (bi >= s0 && bi < s1) srow += v[u];
-        }
+      for (int u = 0; u < 16; u++) {
+        const int bi = bb + u;
+        tot += v[u];
+        if (bi < b) pre += v[u];
+        if (bi >= s0 && bi < s1) srow += v[u];
       }
-      for (; bb < bb1; bb++) {
-        const int v = blk_cnt[(int64_t)bb * E + e];
-        tot += v;
-        if (bb < b) pre += v;
-        if (bb >= s0 && bb < s1) srow += v;
-      }
-      part_tot[sl * E + e] = tot;
-      part_pre[sl * E + e] = pre;
-      part_src[sl * E + e] = srow;
     }
+  }
+  int ev = 0;
+  if (b == 0)
+    for (int bb = tid; bb < B; bb += BLK) ev |= blk_err[bb];
+  const int rv = (c == 0 && tid < CB * R) ? blk_rank[(int64_t)s0 * R + tid] : 0;
+  __syncthreads();  // rsum zeroed, sidx staged
+  if (c == 0) {
+    if (tid < CB * R) atomicAdd(&rsum[tid % R], rv);
+    for (int q = tid + BLK; q < CB * R; q += BLK) atomicAdd(&rsum[q % R], blk_rank[(int64_t)s0 * R + q]);
+  }
+  if (sl < S) {
+    part_tot[sl * E + e_a] = tot;
+    part_pre[sl * E + e_a] = pre;
+    part_src[sl * E + e_a] = srow;
   }
   __syncthreads();
   // (b) thread tid < E owns expert tid: reduce the slices, then a padded
   //     exclusive scan over experts across the whole block
-  int tot = 0, pre = 0, srow = 0;
+  tot = 0;
+  pre = 0;
+  srow = 0;
   if (tid < E) {
-    for (int sl = 0; sl < S; sl++) {
-      tot += part_tot[sl * E + tid];
-      pre += part_pre[sl * E + tid];
-      srow += part_src[sl * E + tid];
+    for (int k = 0; k < S; k++) {
+      tot += part_tot[k * E + tid];
+      pre += part_pre[k * E + tid];
+      srow += part_src[k * E + tid];
     }
   }
   const int padded = (tid < E) ? (tot + A - 1) / A * A : 0;
@@ -288,45 +342,45 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
 #pragma unroll
     for (int ww = 0; ww < kAssignWaves; ww++) masks[ww * E + tid] = 0ull;
   }
-  if (c == 0) {
-    for (int r = tid; r < R; r += kAssignThreads) {
-      int v = 0;
-      for (int bb = s0; bb < s1; bb++) v += blk_rank[(int64_t)bb * R + r];
-      num_tokens_per_rank[(int64_t)src * R + r] = v;
-    }
-  }
+  if (c == 0)
+    for (int r = tid; r < R; r += BLK) num_tokens_per_rank[(int64_t)src * R + r] = rsum[r];
   if (b == 0) {
-    int ev = 0;
-    for (int bb = tid; bb < B; bb += kAssignThreads) ev |= blk_err[bb];
     ev = __syncthreads_or(ev);
     if (tid == 0) *err_word = ev ? EP_LAYOUT_ERR_INDEX : 0;
   }
   __syncthreads();
 
-  // (d) stable ranks
+  // (d) stable ranks, tile by tile (one tile unless the chunk is very large)
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int r0 = 0; r0 < np; r0 += kAssignThreads) {
-    const int p = r0 + tid;
-    int e = e_first;
-    if (r0 > 0) e = (p < np) ? topk_idx[p0 + p] : -1;
-    const bool ok = (e >= 0 && e < E);
-    if (ok) atomicOr(&masks[w * E + e], 1ull << lane);
-    __syncthreads();
-    int slot = -1;
-    unsigned long long m = 0;
-    if (ok) {
-      m = masks[w * E + e];
-      int pw = 0;
-      for (int w2 = 0; w2 < w; w2++) pw += __popcll(masks[w2 * E + e]);
-      slot = base[e] + pw + __popcll(m & below);
+  for (int tt = t0; tt < t1; tt += tok_tile) {
+    const int n = min(tok_tile, t1 - tt) * K;
+    if (tt != t0) {
+      __syncthreads();
+      stage_idx<BLK, kAssignTile>(sidx, topk_idx + (int64_t)tt * K, n);
+      __syncthreads();
     }
-    __syncthreads();
-    if (ok && (m & below) == 0ull) {  // lowest lane of this expert in this wave
-      atomicAdd(&base[e], __popcll(m));
-      masks[w * E + e] = 0ull;
+    for (int r0 = 0; r0 < n; r0 += BLK) {
+      const int p = r0 + tid;
+      const int e = (p < n) ? sidx[p] : -1;
+      const bool ok = (e >= 0 && e < E);
+      if (ok) atomicOr(&masks[w * E + e], 1ull << lane);
+      __syncthreads();
+      int slot = -1;
+      unsigned long long m = 0;
+      if (ok) {
+        m = masks[w * E + e];
+        int pw = 0;
+        for (int w2 = 0; w2 < w; w2++) pw += __popcll(masks[w2 * E + e]);
+        slot = base[e] + pw + __popcll(m & below);
+      }
+      __syncthreads();
+      if (ok && (m & below) == 0ull) {  // lowest lane of this expert in this wave
+        atomicAdd(&base[e], __popcll(m));
+        masks[w * E + e] = 0ull;
+      }
+      __syncthreads();
+      if (p < n) slot_of[(int64_t)tt * K + p] = slot;
     }
-    __syncthreads();
-    if (p < np) slot_of[p0 + p] = slot;
   }
 }
 
@@ -872,10 +926,11 @@ int ep_get_layout(const ep_problem_t* p, const int32_t* topk_idx, int32_t* num_t
                                                 num_recv_per_expert, expert_slot_offset, E, R);
     return check_launch("layout_empty");
   }
-  layout_count_kernel<<<pl.B, kThreads, 0, st>>>(topk_idx, is_token_in_rank, blk_cnt, blk_rank,
+  layout_count_kernel<<<pl.B, kCountThreads, 0, st>>>(topk_idx, is_token_in_rank, blk_cnt, blk_rank,
                                                  blk_err, K, E, R, L, T, pl.CB, pl.C);
   if ((rc = check_launch("layout_count")) != EP_OK) return rc;
-  const size_t mask_bytes = sizeof(unsigned long long) * kAssignWaves * (size_t)E;
+  size_t mask_bytes = sizeof(unsigned long long) * kAssignWaves * (size_t)E;
+  if (mask_bytes < 3 * sizeof(int) * kAssignThreads) mask_bytes = 3 * sizeof(int) * kAssignThreads;
   layout_assign_kernel<<<pl.B, kAssignThreads, mask_bytes, st>>>(
       topk_idx, blk_cnt, blk_rank, blk_err, err, num_tokens_per_rank, num_tokens_per_expert,
       num_recv_per_expert, expert_slot_offset, slot_of, K, E, R, T, pl.CB, pl.C, pl.B,
