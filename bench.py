@@ -2,7 +2,10 @@
 """Benchmark: MoE dispatch + combine on one MI355X, virtual EP ranks.
 
 A step is one pass of the whole hot path over one batch: ep_get_layout ->
-ep_dispatch -> ep_combine, inputs resident in HBM.  The default workload is the
+ep_dispatch -> ep_combine, inputs resident in HBM.  The three calls only
+enqueue kernels, so by default the step is captured once into a HIP graph and
+the timed region replays one HIP graph of the K steps (--eager launches every
+call from Python instead).  The default workload is the
 prefill shape: 4096 tokens x hidden 7168 bf16, 256 experts in 8 groups, top-4
 groups then top-8 experts, 8 virtual ranks, expert_alignment 128.  Expert
 outputs are a separate seeded bf16 buffer (what an expert GEMM would have
@@ -202,6 +205,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget; 0 skips it")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call from Python instead of replaying a HIP graph")
     ap.add_argument("--summarize", action="store_true",
                     help="write profiles/ summaries from rocprofv3 output dirs and exit")
     ap.add_argument("--trace-dir")
@@ -249,36 +254,71 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    def capture(fn, reps):
+        """HIP graph of `reps` back-to-back calls of fn (the library only
+        enqueues kernels on the current stream, so the calls capture)."""
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for _ in range(reps):
+                    fn()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        return g
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
+    if not args.eager:
+        # one graph holding the W warmup steps, one holding the K timed steps
+        warm_graph = capture(step, max(args.warmup, 1))
+        timed_graph = capture(step, args.steps)
+        warm_graph.replay()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps "
+          f"({'eager' if args.eager else 'one HIP graph of K steps'})", file=sys.stderr,
           flush=True)
     # The timed region: K back-to-back steps, nothing else enqueued between them.
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0.record()
-    for i in range(args.steps):
-        step()
+    if args.eager:
+        for i in range(args.steps):
+            step()
+    else:
+        timed_graph.replay()
     g1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
     gpu_step_ms = g0.elapsed_time(g1) / args.steps
+
     # Per-kernel durations: each kernel launched `steps` times back to back
-    # between two events on the stream the library launches on (the inputs of
-    # every launch are the ones the timed steps used).
+    # (one HIP graph of `steps` launches, replayed between two events on the
+    # stream the library launches on), with the inputs the timed steps used.
     def per_launch_ms(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
+        reps = args.steps
+        if args.eager:
             fn()
-        e1.record()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+        else:
+            g = capture(fn, reps)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        return e0.elapsed_time(e1) / reps
 
     lay_ms = per_launch_ms(lambda: ep.get_layout(idx, w.E, w.R, w.A, out=lay))
     dis_ms = per_launch_ms(lambda: ep.dispatch(x, wts, lay, w.fp8, out=recv))
@@ -319,6 +359,7 @@ def main():
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": total_b,
         "gpu_ms_per_step": round(gpu_step_ms, 4),
+        "launch": "eager" if args.eager else "one captured HIP graph of the K steps",
         "kernel_ms": {"layout": round(lay_ms, 4), "dispatch": round(dis_ms, 4),
                       "combine": round(com_ms, 4)},
         "kernel_gbs": {"dispatch": round(disp_b / (dis_ms * 1e-3) / 1e9, 1),

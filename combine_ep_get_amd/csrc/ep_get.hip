@@ -147,19 +147,21 @@ constexpr int kAssignTile = 4096;       // pairs staged per tile in phase 2 (16 
 constexpr int kCountThreads = 512;
 constexpr int kFlagBytes = 16384;       // LDS for is_token_in_rank staging
 
-// stage n <= TILE consecutive pairs of topk_idx into sidx[0, n)
+// Load n (1 <= n <= TILE) consecutive pairs of topk_idx into registers without
+// branches (the index is clamped, so every lane issues its loads back to
+// back), then store them to sidx[0, n).
 template <int BLK, int TILE>
-__device__ __forceinline__ void stage_idx(int* __restrict__ sidx, const int32_t* __restrict__ idx,
+__device__ __forceinline__ void load_idx(int (&v)[TILE / BLK], const int32_t* __restrict__ idx,
+                                         int n) {
+#pragma unroll
+  for (int j = 0; j < TILE / BLK; j++) v[j] = idx[min(j * BLK + (int)threadIdx.x, n - 1)];
+}
+
+template <int BLK, int TILE>
+__device__ __forceinline__ void store_idx(int* __restrict__ sidx, const int (&v)[TILE / BLK],
                                           int n) {
-  constexpr int kPer = TILE / BLK;
-  int v[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; j++) {
-    const int q = j * BLK + (int)threadIdx.x;
-    v[j] = (q < n) ? idx[q] : -1;
-  }
-#pragma unroll
-  for (int j = 0; j < kPer; j++) {
+  for (int j = 0; j < TILE / BLK; j++) {
     const int q = j * BLK + (int)threadIdx.x;
     if (q < n) sidx[q] = v[j];
   }
@@ -174,9 +176,10 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
   __shared__ int sidx[kCountTile];
   __shared__ int hist[EP_MAX_EXPERTS];
   __shared__ int rcnt[EP_MAX_RANKS];
-  __shared__ uint8_t flags[kFlagBytes];
+  __shared__ uint32_t flagw[kFlagBytes / 4];
   __shared__ int err;
   constexpr int BLK = kCountThreads;
+  uint8_t* flags = reinterpret_cast<uint8_t*>(flagw);
   const int tid = threadIdx.x;
   const int b = blockIdx.x, src = b / CB, c = b % CB;
   const int t0 = src * T + c * C;
@@ -189,28 +192,42 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
   for (int tt = t0; tt < t1; tt += tok_tile) {
     const int ntok = min(tok_tile, t1 - tt);
     const int n = ntok * K;
+    int v[kCountTile / BLK];
+    load_idx<BLK, kCountTile>(v, topk_idx + (int64_t)tt * K, n);
     __syncthreads();  // previous tile fully consumed; counters initialised
-    stage_idx<BLK, kCountTile>(sidx, topk_idx + (int64_t)tt * K, n);
-    __syncthreads();
-    for (int q = tid; q < n; q += BLK) {
-      const int e = sidx[q];
-      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-      else if (e != -1) err = EP_LAYOUT_ERR_INDEX;
+    store_idx<BLK, kCountTile>(sidx, v, n);
+#pragma unroll
+    for (int j = 0; j < kCountTile / BLK; j++) {
+      const int e = v[j];
+      if (j * BLK + tid < n) {
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+        else if (e != -1) err = EP_LAYOUT_ERR_INDEX;
+      }
     }
     for (int sub = 0; sub < ntok; sub += tok_sub) {
       const int nt = min(tok_sub, ntok - sub);
-      for (int q = tid; q < nt * R; q += BLK) flags[q] = 0;
+      for (int q = tid; q < (nt * R + 3) / 4; q += BLK) flagw[q] = 0u;
       __syncthreads();
       for (int q = tid; q < nt * K; q += BLK) {
         const int e = sidx[sub * K + q];
         if (e >= 0 && e < E) flags[(q / K) * R + e / L] = 1;
       }
       __syncthreads();
+      // is_token_in_rank rows: 4 bytes per store when rows are word aligned
       uint8_t* out = in_rank + (int64_t)(tt + sub) * R;
-      for (int q = tid; q < nt * R; q += BLK) {
-        const uint8_t v = flags[q];
-        out[q] = v;
-        if (v) atomicAdd(&rcnt[q % R], 1);
+      if ((R & 3) == 0 && (reinterpret_cast<uintptr_t>(in_rank) & 3) == 0) {
+        for (int q = tid; q < nt * R / 4; q += BLK)
+          reinterpret_cast<uint32_t*>(out)[q] = flagw[q];
+      } else {
+        for (int q = tid; q < nt * R; q += BLK) out[q] = flags[q];
+      }
+      // per-rank token counts: thread (r, slice) sums a column, one atomic each
+      const int slices = BLK / R;  // R <= 256 so at least 2
+      if (tid < slices * R) {
+        const int r = tid % R, sl = tid / R;
+        int cnt = 0;
+        for (int t = sl; t < nt; t += slices) cnt += flags[t * R + r];
+        if (cnt) atomicAdd(&rcnt[r], cnt);
       }
       __syncthreads();
     }
@@ -266,34 +283,45 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
   const int tok_tile = kAssignTile / K;
   const int s0 = src * CB, s1 = s0 + CB;
 
-  // (a) loads: the first tile of routing indices, the per-block histogram
-  //     slices, the per-source rank counts (first block of a source) and the
-  //     error flags (block 0), all issued before anything waits on them
+  // (a) loads, all issued before any is consumed and without branches (the
+  //     addresses are clamped, the results masked): the first tile of routing
+  //     indices, 16 per-block histogram entries per thread (one slice of the
+  //     blocks for one expert), the per-source rank counts and the error flags
+  constexpr int kPer = kAssignTile / BLK;
   const int ntok0 = min(tok_tile, t1 - t0);
-  stage_idx<BLK, kAssignTile>(sidx, topk_idx + (int64_t)t0 * K, ntok0 * K);
-  for (int r = tid; r < R; r += BLK) rsum[r] = 0;
+  const int n0 = ntok0 * K;
+  int iv[kPer];
+  load_idx<BLK, kAssignTile>(iv, topk_idx + (int64_t)t0 * K, n0);
   const int S = BLK / E;  // slices of the block range per expert
   const int e_a = tid % E, sl = tid / E;
+  const int bb0 = sl < S ? (int)((int64_t)B * sl / S) : 0;
+  const int bb1 = sl < S ? (int)((int64_t)B * (sl + 1) / S) : 0;
+  int cv[16];
+#pragma unroll
+  for (int u = 0; u < 16; u++) cv[u] = blk_cnt[(int64_t)min(bb0 + u, B - 1) * E + e_a];
+  const int rv = blk_rank[(int64_t)s0 * R + min(tid, CB * R - 1)];
+  const int evv = blk_err[min(tid, B - 1)];
+  // consume
+  store_idx<BLK, kAssignTile>(sidx, iv, n0);
+  for (int r = tid; r < R; r += BLK) rsum[r] = 0;
   int tot = 0, pre = 0, srow = 0;
-  if (sl < S) {
-    const int bb0 = (int)((int64_t)B * sl / S), bb1 = (int)((int64_t)B * (sl + 1) / S);
-    for (int bb = bb0; bb < bb1; bb += 16) {
-      int v[16];
 #pragma unroll
-      for (int u = 0; u < 16; u++) v[u] = (bb + u < bb1) ? blk_cnt[(int64_t)(bb + u) * E + e_a] : 0;
-#pragma unroll
-      for (int u = 0; u < 16; u++) {
-        const int bi = bb + u;
-        tot += v[u];
-        if (bi < b) pre += v[u];
-        if (bi >= s0 && bi < s1) srow += v[u];
-      }
-    }
+  for (int u = 0; u < 16; u++) {
+    const int bi = bb0 + u;
+    const int v = (bi < bb1) ? cv[u] : 0;
+    tot += v;
+    if (bi < b) pre += v;
+    if (bi >= s0 && bi < s1) srow += v;
   }
-  int ev = 0;
+  for (int bi = bb0 + 16; bi < bb1; bi++) {  // only when a slice spans more than 16 blocks
+    const int v = blk_cnt[(int64_t)bi * E + e_a];
+    tot += v;
+    if (bi < b) pre += v;
+    if (bi >= s0 && bi < s1) srow += v;
+  }
+  int ev = (b == 0 && tid < B) ? evv : 0;
   if (b == 0)
-    for (int bb = tid; bb < B; bb += BLK) ev |= blk_err[bb];
-  const int rv = (c == 0 && tid < CB * R) ? blk_rank[(int64_t)s0 * R + tid] : 0;
+    for (int bb = tid + BLK; bb < B; bb += BLK) ev |= blk_err[bb];
   __syncthreads();  // rsum zeroed, sidx staged
   if (c == 0) {
     if (tid < CB * R) atomicAdd(&rsum[tid % R], rv);
@@ -355,8 +383,10 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
   for (int tt = t0; tt < t1; tt += tok_tile) {
     const int n = min(tok_tile, t1 - tt) * K;
     if (tt != t0) {
+      int v[kPer];
+      load_idx<BLK, kAssignTile>(v, topk_idx + (int64_t)tt * K, n);
       __syncthreads();
-      stage_idx<BLK, kAssignTile>(sidx, topk_idx + (int64_t)tt * K, n);
+      store_idx<BLK, kAssignTile>(sidx, v, n);
       __syncthreads();
     }
     for (int r0 = 0; r0 < n; r0 += BLK) {
@@ -381,6 +411,171 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
       __syncthreads();
       if (p < n) slot_of[(int64_t)tt * K + p] = slot;
     }
+  }
+}
+
+// Single-launch layout for problems with N*K <= kFusedMaxPairs, N <= kFlagBytes
+// and E <= kFusedMaxExperts (the decode-sized workloads).
+// No block needs another block's results: each block reads all N*K routing
+// indices (from L2 after the first touch) and files every pair into one of
+// four histograms by the position of its token: before the block's source,
+// in the source before the block's chunk, from the chunk to the end of the
+// source, after the source.  The first two give the block's prefix, all four
+// the totals, the middle two the source's row of num_tokens_per_expert.  The
+// same pass marks is_token_in_rank for every token of the block's source in
+// LDS (N bytes at most), so the first block of a source also counts its rank
+// row.  Then the padded scan, publishing and stable ranks run as in phase 2.
+// Problems up to this many (token, k) pairs take the single-launch layout
+// (measured on MI355X: 5.0 us at 256 pairs, 6.7 us at 8192, 10.8 us at 32768,
+// where the two-launch layout costs 10.2-10.5 us throughout).
+#ifndef EP_FUSED_MAX_PAIRS
+#define EP_FUSED_MAX_PAIRS 16384
+#endif
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedMaxPairs = EP_FUSED_MAX_PAIRS;
+constexpr int kFusedMaxExperts = 512;
+
+__global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
+    const int32_t* __restrict__ topk_idx, uint8_t* __restrict__ in_rank,
+    int32_t* __restrict__ err_word, int32_t* __restrict__ num_tokens_per_rank,
+    int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_recv,
+    int32_t* __restrict__ off, int32_t* __restrict__ slot_of, int N, int K, int E, int R, int L,
+    int T, int CB, int C, int A) {
+  constexpr int BLK = kFusedThreads;
+  constexpr int kWv = BLK / 64;
+  __shared__ int sidx[kAssignTile];
+  __shared__ int hist[4][kFusedMaxExperts];
+  __shared__ int base[kFusedMaxExperts];
+  __shared__ short srank[kFusedMaxExperts];
+  __shared__ int rsum[EP_MAX_RANKS];
+  __shared__ uint32_t flagw[kFlagBytes / 4];
+  __shared__ int wsum[kWv];
+  __shared__ int err;
+  extern __shared__ unsigned long long masks[];  // [kWv][E]
+  uint8_t* flags = reinterpret_cast<uint8_t*>(flagw);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = blockIdx.x, src = b / CB, c = b % CB;
+  const int t0 = src * T + c * C;
+  const int t1 = src * T + min((c + 1) * C, T);
+  const int p0 = t0 * K, np = (t1 - t0) * K;
+
+  // own chunk (<= kAssignTile pairs) first: it is needed last
+  int iv[kAssignTile / BLK];
+  load_idx<BLK, kAssignTile>(iv, topk_idx + p0, np);
+  for (int q = tid; q < 4 * E; q += BLK) (&hist[0][0])[(q / E) * kFusedMaxExperts + q % E] = 0;
+  for (int q = tid; q < (T * R + 3) / 4; q += BLK) flagw[q] = 0u;
+  for (int e = tid; e < E; e += BLK) srank[e] = (short)(e / L);
+  if (tid == 0) err = 0;
+  __syncthreads();
+  store_idx<BLK, kAssignTile>(sidx, iv, np);
+
+  // (a) every pair of the problem, 16 loads in flight per thread; the class
+  //     comes from comparing the pair's position with the (token-aligned)
+  //     class boundaries, the expert -> rank map from an LDS table
+  const int NK = N * K, ps0 = src * T * K, ps1 = ps0 + T * K;
+  for (int pb = 0; pb < NK; pb += 16 * BLK) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; u++) v[u] = topk_idx[min(pb + u * BLK + tid, NK - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; u++) {
+      const int p = pb + u * BLK + tid;
+      const int e = v[u];
+      if (p < NK) {
+        if (e >= 0 && e < E) {
+          const int cls = (p >= ps0) + (p >= p0) + (p >= ps1);
+          atomicAdd(&hist[cls][e], 1);
+          if (cls == 1 || cls == 2) flags[((p - ps0) / K) * R + srank[e]] = 1;
+        } else if (e != -1) {
+          err = EP_LAYOUT_ERR_INDEX;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // (b) prefix, totals, source row; padded exclusive scan over experts
+  int tot = 0, pre = 0, srow = 0;
+  if (tid < E) {
+    const int h0 = hist[0][tid], h1 = hist[1][tid], h2 = hist[2][tid], h3 = hist[3][tid];
+    pre = h0 + h1;
+    srow = h1 + h2;
+    tot = h0 + h1 + h2 + h3;
+  }
+  const int padded = (tid < E) ? (tot + A - 1) / A * A : 0;
+  int x = padded;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  // is_token_in_rank rows of this chunk, straight from the source's flags
+  {
+    const int fo = (t0 - src * T) * R, nb = (t1 - t0) * R;
+    uint8_t* out = in_rank + (int64_t)t0 * R;
+    if ((fo & 3) == 0 && (nb & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 3) == 0) {
+      for (int q = tid; q < nb / 4; q += BLK) reinterpret_cast<uint32_t*>(out)[q] = flagw[fo / 4 + q];
+    } else {
+      for (int q = tid; q < nb; q += BLK) out[q] = flags[fo + q];
+    }
+  }
+  if (c == 0) {
+    for (int r = tid; r < R; r += BLK) rsum[r] = 0;
+  }
+  __syncthreads();
+  if (c == 0) {  // per-rank token counts of the source: column sums, one atomic each
+    const int slices = BLK / R;
+    if (tid < slices * R) {
+      const int r = tid % R, sl = tid / R;
+      int cnt = 0;
+      for (int t = sl; t < T; t += slices) cnt += flags[t * R + r];
+      if (cnt) atomicAdd(&rsum[r], cnt);
+    }
+  }
+  int wpre = 0;
+  for (int ww = 0; ww < w; ww++) wpre += wsum[ww];
+  const int incl = wpre + x;
+  if (tid < E) {
+    const int offe = incl - padded;
+    if (b == 0) {
+      off[tid] = offe;
+      num_recv[tid] = tot;
+      if (tid == E - 1) off[E] = incl;
+    }
+    if (c == 0) num_tokens_per_expert[(int64_t)src * E + tid] = srow;
+    base[tid] = offe + pre;
+#pragma unroll
+    for (int ww = 0; ww < kWv; ww++) masks[ww * E + tid] = 0ull;
+  }
+  if (b == 0 && tid == 0) *err_word = err;
+  __syncthreads();
+  if (c == 0)
+    for (int r = tid; r < R; r += BLK) num_tokens_per_rank[(int64_t)src * R + r] = rsum[r];
+
+  // (c) stable ranks of this chunk
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int r0 = 0; r0 < np; r0 += BLK) {
+    const int p = r0 + tid;
+    const int e = (p < np) ? sidx[p] : -1;
+    const bool ok = (e >= 0 && e < E);
+    if (ok) atomicOr(&masks[w * E + e], 1ull << lane);
+    __syncthreads();
+    int slot = -1;
+    unsigned long long m = 0;
+    if (ok) {
+      m = masks[w * E + e];
+      int pw = 0;
+      for (int w2 = 0; w2 < w; w2++) pw += __popcll(masks[w2 * E + e]);
+      slot = base[e] + pw + __popcll(m & below);
+    }
+    __syncthreads();
+    if (ok && (m & below) == 0ull) {
+      atomicAdd(&base[e], __popcll(m));
+      masks[w * E + e] = 0ull;
+    }
+    __syncthreads();
+    if (p < np) slot_of[(int64_t)p0 + p] = slot;
   }
 }
 
@@ -925,6 +1120,15 @@ int ep_get_layout(const ep_problem_t* p, const int32_t* topk_idx, int32_t* num_t
     layout_empty_kernel<<<1, kThreads, 0, st>>>(err, num_tokens_per_rank, num_tokens_per_expert,
                                                 num_recv_per_expert, expert_slot_offset, E, R);
     return check_launch("layout_empty");
+  }
+  if ((int64_t)N * K <= kFusedMaxPairs && N <= kFlagBytes && E <= kFusedMaxExperts &&
+      (int64_t)pl.C * K <= kAssignTile) {
+    const size_t mbytes = sizeof(unsigned long long) * (kFusedThreads / 64) * (size_t)E;
+    layout_fused_kernel<<<pl.B, kFusedThreads, mbytes, st>>>(
+        topk_idx, is_token_in_rank, err, num_tokens_per_rank, num_tokens_per_expert,
+        num_recv_per_expert, expert_slot_offset, slot_of, N, K, E, R, L, T, pl.CB, pl.C,
+        p->expert_alignment);
+    return check_launch("layout_fused");
   }
   layout_count_kernel<<<pl.B, kCountThreads, 0, st>>>(topk_idx, is_token_in_rank, blk_cnt, blk_rank,
                                                  blk_err, K, E, R, L, T, pl.CB, pl.C);
