@@ -659,15 +659,17 @@ __global__ __launch_bounds__(BLK) void dispatch_bf16_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
     const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
     u32x4* __restrict__ recv_x, int32_t* __restrict__ recv_src, float* __restrict__ recv_w,
-    int N, int K, int E, int H8, int64_t cap, int tok_blocks) {
+    int N, int K, int E, int H8, int64_t cap, int fill_blocks) {
   __shared__ int s_off[EP_MAX_EXPERTS + 1];
   __shared__ int s_cnt[EP_MAX_EXPERTS];
-  if ((int)blockIdx.x >= tok_blocks) {
-    fill_padding<BLK>(blockIdx.x - tok_blocks, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
+  // the padding-tag blocks come first so that they run alongside the token
+  // blocks instead of after them
+  if ((int)blockIdx.x < fill_blocks) {
+    fill_padding<BLK>(blockIdx.x, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
     return;
   }
   constexpr int kTok = BLK / TPT;
-  const int t = uniform(blockIdx.x * kTok + (int)(threadIdx.x / TPT));
+  const int t = uniform(((int)blockIdx.x - fill_blocks) * kTok + (int)(threadIdx.x / TPT));
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
   const int vl = threadIdx.x % TPT;
@@ -716,15 +718,14 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
     const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
     u32x4* __restrict__ recv_q, float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
-    float* __restrict__ recv_w, int N, int K, int E, int H, int64_t cap, int tok_blocks) {
+    float* __restrict__ recv_w, int N, int K, int E, int H, int64_t cap, int fill_blocks) {
   __shared__ int s_off[EP_MAX_EXPERTS + 1];
   __shared__ int s_cnt[EP_MAX_EXPERTS];
-  if ((int)blockIdx.x >= tok_blocks) {
-    fill_padding<kThreads>(blockIdx.x - tok_blocks, off, recv_cnt, E, cap, recv_src, recv_w,
-                           s_off, s_cnt);
+  if ((int)blockIdx.x < fill_blocks) {
+    fill_padding<kThreads>(blockIdx.x, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
     return;
   }
-  const int t = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  const int t = uniform(((int)blockIdx.x - fill_blocks) * kWaves + (threadIdx.x >> 6));
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
@@ -762,17 +763,33 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
       const float scale = zero ? 1.0f : am / 448.0f;
       const float inv = 448.0f / am;
       u32x4 q;
+      if (!zero && __builtin_isfinite(inv)) {
+        // |f * inv| <= 448 (1 + 2^-23) < 464 here, where the hardware
+        // conversion (v_cvt_pk_fp8_f32, OCP E4M3 with RNE) equals
+        // e4m3_rne_sat bit for bit (checked on all 2^32 inputs)
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-          const float fv = f[4 * j + b];
-          const uint32_t code = zero ? ((__float_as_uint(fv) >> 24) & 0x80u)
-                                     : e4m3_rne_sat(fv * inv);
-          word |= code << (8 * b);
+        for (int j = 0; j < 4; j++) {
+          const float p0 = f[4 * j] * inv, p1 = f[4 * j + 1] * inv;
+          const float p2 = f[4 * j + 2] * inv, p3 = f[4 * j + 3] * inv;
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+          q[j] = (uint32_t)word;
         }
-        q[j] = word;
+      } else {
+        // all-zero group (signed zero codes), or amax so small that 448/amax
+        // overflows: the software encoder saturates as the contract says
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int b = 0; b < 4; b++) {
+            const float fv = f[4 * j + b];
+            const uint32_t code = zero ? ((__float_as_uint(fv) >> 24) & 0x80u)
+                                       : e4m3_rne_sat(fv * inv);
+            word |= code << (8 * b);
+          }
+          q[j] = word;
+        }
       }
       const float sv = __shfl(scale, 8 * (lane & 7));
       if ((lane >> 3) == i) my_scale = sv;
@@ -1023,21 +1040,21 @@ template <int NV>
 void launch_dispatch_bf16(dim3 grid, hipStream_t st, const ep_problem_t* p, const void* x,
                           const float* w, const int32_t* slot_of, const int32_t* off,
                           const int32_t* cnt, void* recv_x, int32_t* recv_src, float* recv_w,
-                          int64_t cap, int tok_blocks) {
+                          int64_t cap, int fill_blocks) {
   constexpr int blk = EP_DISPATCH_TPT > kThreads ? EP_DISPATCH_TPT : kThreads;
   dispatch_bf16_kernel<EP_DISPATCH_TPT, NV, blk><<<grid, blk, 0, st>>>(
       (const u32x4*)x, w, slot_of, off, cnt, (u32x4*)recv_x, recv_src, recv_w, p->num_tokens,
-      p->num_topk, p->num_experts, p->hidden / 8, cap, tok_blocks);
+      p->num_topk, p->num_experts, p->hidden / 8, cap, fill_blocks);
 }
 
 template <int NI>
 void launch_dispatch_fp8(dim3 grid, hipStream_t st, const ep_problem_t* p, const void* x,
                          const float* w, const int32_t* slot_of, const int32_t* off,
                          const int32_t* cnt, void* recv_x, float* recv_scales,
-                         int32_t* recv_src, float* recv_w, int64_t cap, int tok_blocks) {
+                         int32_t* recv_src, float* recv_w, int64_t cap, int fill_blocks) {
   dispatch_fp8_kernel<NI><<<grid, kThreads, 0, st>>>(
       (const u32x4*)x, w, slot_of, off, cnt, (u32x4*)recv_x, recv_scales, recv_src, recv_w,
-      p->num_tokens, p->num_topk, p->num_experts, p->hidden, cap, tok_blocks);
+      p->num_tokens, p->num_topk, p->num_experts, p->hidden, cap, fill_blocks);
 }
 
 template <int Q, bool MULTI>
@@ -1177,7 +1194,7 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
 #define EP_D16(NV)                                                                          \
   launch_dispatch_bf16<NV>(grid, st, p, x, topk_weights, slot_of, expert_slot_offset,      \
                            num_recv_per_expert, recv_x, recv_src_idx, recv_topk_weights,   \
-                           recv_capacity, tok_blocks)
+                           recv_capacity, (int)fill_blocks64)
     if (q <= 1) EP_D16(1);
     else if (q <= 2) EP_D16(2);
     else if (q <= 4) EP_D16(4);
@@ -1193,7 +1210,7 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
 #define EP_D8(NI)                                                                           \
   launch_dispatch_fp8<NI>(grid, st, p, x, topk_weights, slot_of, expert_slot_offset,       \
                           num_recv_per_expert, recv_x, recv_scales, recv_src_idx,          \
-                          recv_topk_weights, recv_capacity, tok_blocks)
+                          recv_topk_weights, recv_capacity, (int)fill_blocks64)
     if (q <= 1) EP_D8(1);
     else if (q <= 2) EP_D8(2);
     else if (q <= 4) EP_D8(4);
