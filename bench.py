@@ -154,6 +154,10 @@ def summarize(args):
     lines.append(f"sum of per-step kernel averages: {step_us:.2f} us")
     open(os.path.join(out_dir, f"kernel_trace_{w.name}.txt"), "w").write("\n".join(lines) + "\n")
 
+    if not (args.fetch_dir and args.write_dir):
+        print(f"wrote the kernel trace summary for {w.name}")
+        return
+
     def per_kernel(path):
         acc = {}
         for r in _csv_rows(path):
