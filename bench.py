@@ -209,6 +209,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget; 0 skips it")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--ll", type=int, default=0, metavar="M",
+                    help="low-latency path: ep_ll_dispatch (routing + payload in one launch, "
+                         "M rows per (expert, source) sub-block) + ep_combine")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying a HIP graph")
     ap.add_argument("--summarize", action="store_true",
@@ -240,23 +243,41 @@ def main():
     wts = torch.from_numpy(inp["topk_weights"]).to(dev)
     x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
     eo = torch.from_numpy(eo_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    lay = ep.alloc_layout(w.N, w.K, w.E, w.R, w.A, dev)
-    recv = ep.alloc_recv(lay, w.H, w.fp8, dev)
     y = torch.empty((w.N, w.H), dtype=torch.bfloat16, device=dev)
+    if args.ll:
+        ll_out = ep.alloc_ll(w.N, w.K, w.E, w.R, args.ll, w.H, w.fp8, dev)
+        lay = ll_out[0]
+        # expert outputs: seeded rows placed at the slots the routing uses (the
+        # sub-blocks' unused rows are never read)
+        ep.ll_dispatch(x, idx, wts, w.E, w.R, args.ll, w.fp8, out=ll_out)
+        used = lay.slot_of.flatten().long()
+        used = used[used >= 0]
+        rows = torch.from_numpy(wl.make_expert_out(w, int(used.numel()), args.seed)
+                                .view(np.int16)).view(torch.bfloat16).to(dev)
+        eo = torch.zeros((lay.capacity, w.H), dtype=torch.bfloat16, device=dev)
+        eo.index_copy_(0, used, rows)
+    else:
+        lay = ep.alloc_layout(w.N, w.K, w.E, w.R, w.A, dev)
+        recv = ep.alloc_recv(lay, w.H, w.fp8, dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    def do_layout():
         ep.get_layout(idx, w.E, w.R, w.A, out=lay)
-        if ev is not None:
-            ev[1].record()
-        ep.dispatch(x, wts, lay, w.fp8, out=recv)
-        if ev is not None:
-            ev[2].record()
+
+    def do_dispatch():
+        if args.ll:
+            ep.ll_dispatch(x, idx, wts, w.E, w.R, args.ll, w.fp8, out=ll_out)
+        else:
+            ep.dispatch(x, wts, lay, w.fp8, out=recv)
+
+    def do_combine():
         ep.combine(eo, lay, wts, out=y)
-        if ev is not None:
-            ev[3].record()
+
+    def step():
+        if not args.ll:
+            do_layout()
+        do_dispatch()
+        do_combine()
 
     def capture(fn, reps):
         """HIP graph of `reps` back-to-back calls of fn (the library only
@@ -324,9 +345,9 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    lay_ms = per_launch_ms(lambda: ep.get_layout(idx, w.E, w.R, w.A, out=lay))
-    dis_ms = per_launch_ms(lambda: ep.dispatch(x, wts, lay, w.fp8, out=recv))
-    com_ms = per_launch_ms(lambda: ep.combine(eo, lay, wts, out=y))
+    lay_ms = 0.0 if args.ll else per_launch_ms(do_layout)
+    dis_ms = per_launch_ms(do_dispatch)
+    com_ms = per_launch_ms(do_combine)
 
     disp_b, comb_b = algorithmic_bytes(w)
     total_b = disp_b + comb_b
@@ -334,6 +355,8 @@ def main():
     if dis_ms >= com_ms:
         dom_b, dom_ms = disp_b, dis_ms
         dom_kernel = "dispatch_fp8" if w.fp8 else "dispatch_bf16"
+        if args.ll:
+            dom_kernel = "ll_dispatch_fp8" if w.fp8 else "ll_dispatch_bf16"
     else:
         dom_b, dom_ms = comb_b, com_ms
         dom_kernel = "combine"
@@ -357,7 +380,9 @@ def main():
                                f"top-{w.K}, {w.R} virtual ranks, expert_alignment {w.A}, "
                                f"{'e4m3' if w.fp8 else 'bf16'} dispatch, {w.routing} routing",
                    "num_tokens": w.N, "hidden": w.H, "num_experts": w.E, "num_topk": w.K,
-                   "num_ranks": w.R, "expert_alignment": w.A, "seed": args.seed,
+                   "num_ranks": w.R, "expert_alignment": 1 if args.ll else w.A,
+                   "seed": args.seed, "path": (f"low-latency (M={args.ll})" if args.ll
+                                               else "layout + dispatch + combine"),
                    "parallelism": "1 GPU, virtual EP ranks"},
         "tokens_per_s": round(w.N / step_s, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),

@@ -42,7 +42,8 @@ class EPError(RuntimeError):
 
 
 EXPORTS = ("ep_recv_capacity", "ep_workspace_bytes", "ep_get_layout", "ep_dispatch",
-           "ep_combine", "ep_layout_error", "ep_status_str")
+           "ep_combine", "ep_layout_error", "ep_status_str", "ep_ll_capacity", "ep_ll_dispatch")
+EP_LAYOUT_ERR_OVERFLOW = 2
 
 
 def lib():
@@ -82,6 +83,10 @@ def load(path):
     L.ep_layout_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
     L.ep_status_str.restype = ctypes.c_char_p
     L.ep_status_str.argtypes = [ctypes.c_int]
+    L.ep_ll_capacity.restype = i64
+    L.ep_ll_capacity.argtypes = [P, ctypes.c_int32]
+    L.ep_ll_dispatch.restype = ctypes.c_int
+    L.ep_ll_dispatch.argtypes = [P, ctypes.c_int32] + [vp] * 10 + [vp]
     return L
 
 
@@ -257,3 +262,81 @@ def layout_error(layout):
     _check("ep_layout_error", lib().ep_layout_error(_ptr(layout.workspace), ctypes.byref(v),
                                                     _stream()))
     return int(v.value)
+
+
+# ------------------------------------------------------------ low latency
+@dataclass
+class LLLayout:
+    """Output of ll_dispatch's routing half: recv_count [E, R] (rows used per
+    (expert, source) sub-block of M rows), slot_of [N, K] (the handle for
+    combine), flags [R] (per-source EP_LAYOUT_ERR_* bits)."""
+    num_tokens: int
+    num_topk: int
+    num_experts: int
+    num_ranks: int
+    max_tokens_per_rank: int
+    capacity: int
+    recv_count: object
+    slot_of: object
+    flags: object
+    expert_alignment: int = 1
+
+    def problem(self, hidden=8, use_fp8=False):
+        return problem(self.num_tokens, hidden, self.num_topk, self.num_experts,
+                       self.num_ranks, 1, use_fp8)
+
+
+def ll_capacity(num_tokens, num_topk, num_experts, num_ranks, max_tokens_per_rank):
+    p = problem(num_tokens, 8, num_topk, num_experts, num_ranks, 1)
+    v = lib().ep_ll_capacity(ctypes.byref(p), int(max_tokens_per_rank))
+    if v < 0:
+        raise ValueError("invalid problem sizes")
+    return int(v)
+
+
+def alloc_ll(num_tokens, num_topk, num_experts, num_ranks, max_tokens_per_rank, hidden,
+             use_fp8=False, device="cuda"):
+    """Allocate the low-latency layout and receive buffers."""
+    import torch
+    N, K, E, R, M = num_tokens, num_topk, num_experts, num_ranks, max_tokens_per_rank
+    cap = ll_capacity(N, K, E, R, M)
+    lay = LLLayout(N, K, E, R, M, cap,
+                   torch.empty((E, R), dtype=torch.int32, device=device),
+                   torch.empty((N, K), dtype=torch.int32, device=device),
+                   torch.empty((R,), dtype=torch.int32, device=device))
+    return lay, alloc_recv(lay, hidden, use_fp8, device)
+
+
+def ll_dispatch(x, topk_idx, topk_weights, num_experts, num_ranks, max_tokens_per_rank,
+                use_fp8=False, out=None, with_meta=True):
+    """Routing and payload in one launch (see ep_ll_dispatch).
+
+    Returns (layout, (recv_x, recv_scales, recv_src_idx, recv_topk_weights)).
+    ``out`` is a pair from alloc_ll for allocation-free calls."""
+    import torch
+    N, H = x.shape
+    K = topk_idx.shape[1]
+    if out is None:
+        out = alloc_ll(N, K, num_experts, num_ranks, max_tokens_per_rank, H, use_fp8, x.device)
+    lay, recv = out
+    if (lay.num_tokens, lay.num_topk, lay.num_experts, lay.num_ranks,
+            lay.max_tokens_per_rank) != (N, K, num_experts, num_ranks, max_tokens_per_rank):
+        raise ValueError("ll_dispatch: `out` was allocated for another problem")
+    _need(x, torch.bfloat16, (N, H), "x")
+    _need(topk_idx, torch.int32, (N, K), "topk_idx")
+    recv_x, scales, src, rw = recv
+    _need(recv_x, torch.float8_e4m3fn if use_fp8 else torch.bfloat16, (lay.capacity, H), "recv_x")
+    if use_fp8:
+        _need(scales, torch.float32, (lay.capacity, H // 128), "recv_scales")
+    if with_meta:
+        _need(src, torch.int32, (lay.capacity,), "recv_src_idx")
+        _need(rw, torch.float32, (lay.capacity,), "recv_topk_weights")
+        _need(topk_weights, torch.float32, (N, K), "topk_weights")
+    p = problem(N, H, K, num_experts, num_ranks, 1, use_fp8)
+    rc = lib().ep_ll_dispatch(ctypes.byref(p), int(max_tokens_per_rank), _ptr(topk_idx), _ptr(x),
+                              _ptr(topk_weights if with_meta else None), _ptr(lay.recv_count),
+                              _ptr(lay.slot_of), _ptr(lay.flags), _ptr(recv_x),
+                              _ptr(scales if use_fp8 else None), _ptr(src if with_meta else None),
+                              _ptr(rw if with_meta else None), _stream())
+    _check("ep_ll_dispatch", rc)
+    return lay, (recv_x, scales if use_fp8 else None, src, rw)

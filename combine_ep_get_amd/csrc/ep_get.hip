@@ -62,9 +62,6 @@ namespace {
 #ifndef EP_BLOCK
 #define EP_BLOCK 256
 #endif
-#ifndef EP_DISPATCH_KINNER
-#define EP_DISPATCH_KINNER 0
-#endif
 constexpr int kThreads = EP_BLOCK;        // threads per block of the row kernels
 constexpr int kWaves = kThreads / 64;
 constexpr int kFillPerThread = 8;         // padding-fill: slots per thread
@@ -651,6 +648,34 @@ __device__ __forceinline__ void write_meta(int t, int K, int lane, int myslot,
   }
 }
 
+// Copy one bf16 row (H8 16-byte chunks) to the slots that lanes 0..K-1 of
+// `myslot` name (-1: none).  TPT threads share the row; `vl` is this thread's
+// index among them.  The row is read once into VGPRs per pass of NV chunks per
+// thread and stored to every slot.
+template <int TPT, int NV>
+__device__ __forceinline__ void copy_row_bf16(const u32x4* __restrict__ row,
+                                              u32x4* __restrict__ recv_x, int myslot, int K,
+                                              int H8, int vl) {
+  for (int base = 0; base < H8; base += TPT * NV) {
+    u32x4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int c = base + i * TPT + vl;
+      if (c < H8) v[i] = ld16<EP_DISPATCH_NT_LOAD>(row + c);
+    }
+    for (int k = 0; k < K; k++) {
+      const int s = lane_value(myslot, k);
+      if (s < 0) continue;
+      u32x4* dst = recv_x + (int64_t)s * H8;
+#pragma unroll
+      for (int i = 0; i < NV; i++) {
+        const int c = base + i * TPT + vl;
+        if (c < H8) st16(dst + c, v[i]);
+      }
+    }
+  }
+}
+
 // bf16 rows: TPT threads (a multiple of 64) per token; NV 16-byte chunks per
 // thread per pass, so one pass moves TPT*NV*16 bytes of the row, which is read
 // once into VGPRs and then stored to each of the token's K slots.
@@ -674,63 +699,19 @@ __global__ __launch_bounds__(BLK) void dispatch_bf16_kernel(
   const int lane = threadIdx.x & 63;
   const int vl = threadIdx.x % TPT;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
-  const u32x4* row = x + (int64_t)t * H8;
-  for (int base = 0; base < H8; base += TPT * NV) {
-    u32x4 v[NV];
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-      const int c = base + i * TPT + vl;
-      if (c < H8) v[i] = ld16<EP_DISPATCH_NT_LOAD>(row + c);
-    }
-#if EP_DISPATCH_KINNER
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-      const int c = base + i * TPT + vl;
-      for (int k = 0; k < K; k++) {
-        const int s = lane_value(myslot, k);
-        if (s < 0) continue;
-        if (c < H8) st16(recv_x + (int64_t)s * H8 + c, v[i]);
-      }
-    }
-#else
-    for (int k = 0; k < K; k++) {
-      const int s = lane_value(myslot, k);
-      if (s < 0) continue;
-      u32x4* dst = recv_x + (int64_t)s * H8;
-#pragma unroll
-      for (int i = 0; i < NV; i++) {
-        const int c = base + i * TPT + vl;
-        if (c < H8) st16(dst + c, v[i]);
-      }
-    }
-#endif
-  }
+  copy_row_bf16<TPT, NV>(x + (int64_t)t * H8, recv_x, myslot, K, H8, vl);
   if (vl < 64) write_meta(t, K, lane, myslot, w, recv_src, recv_w);
 }
 
-// e4m3 rows: one wavefront per token.  A lane owns 16 consecutive channels
-// (two 16-byte bf16 loads, one 16-byte code store); 8 lanes form a
-// 128-channel group whose amax is reduced with xor-shuffles.  NI iterations
-// of 1024 channels per pass.  After iteration i, lanes 8i..8i+7 pick up the
-// scales of groups 8i..8i+7 so that one store per slot writes 64 scales.
+// Quantise one bf16 row of H channels (H % 128 == 0) to E4M3 with one fp32
+// scale per 128-channel group and store codes and scales to the slots that
+// lanes 0..K-1 of `myslot` name; one wavefront per row.
 template <int NI>
-__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
-    const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
-    const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
-    u32x4* __restrict__ recv_q, float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
-    float* __restrict__ recv_w, int N, int K, int E, int H, int64_t cap, int fill_blocks) {
-  __shared__ int s_off[EP_MAX_EXPERTS + 1];
-  __shared__ int s_cnt[EP_MAX_EXPERTS];
-  if ((int)blockIdx.x < fill_blocks) {
-    fill_padding<kThreads>(blockIdx.x, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
-    return;
-  }
-  const int t = uniform(((int)blockIdx.x - fill_blocks) * kWaves + (threadIdx.x >> 6));
-  if (t >= N) return;
-  const int lane = threadIdx.x & 63;
-  const int myslot = load_slot(slot_of, t, K, lane, cap);
-  const int H8 = H >> 3, H16 = H >> 4, G = H >> 7;
-  const u32x4* row = x + (int64_t)t * H8;
+__device__ __forceinline__ void quant_row_fp8(const u32x4* __restrict__ row,
+                                              u32x4* __restrict__ recv_q,
+                                              float* __restrict__ recv_scales, int myslot, int K,
+                                              int H, int lane) {
+  const int H16 = H >> 4, G = H >> 7;
   for (int pbase = 0; pbase < H; pbase += NI * 1024) {
     u32x4 v[NI][2];
 #pragma unroll
@@ -810,7 +791,126 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
       }
     }
   }
+}
+
+// e4m3 rows: one wavefront per token.  A lane owns 16 consecutive channels
+// (two 16-byte bf16 loads, one 16-byte code store); 8 lanes form a
+// 128-channel group whose amax is reduced with xor-shuffles.  NI iterations
+// of 1024 channels per pass.  After iteration i, lanes 8i..8i+7 pick up the
+// scales of groups 8i..8i+7 so that one store per slot writes 64 scales.
+template <int NI>
+__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
+    u32x4* __restrict__ recv_q, float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
+    float* __restrict__ recv_w, int N, int K, int E, int H, int64_t cap, int fill_blocks) {
+  __shared__ int s_off[EP_MAX_EXPERTS + 1];
+  __shared__ int s_cnt[EP_MAX_EXPERTS];
+  if ((int)blockIdx.x < fill_blocks) {
+    fill_padding<kThreads>(blockIdx.x, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
+    return;
+  }
+  const int t = uniform(((int)blockIdx.x - fill_blocks) * kWaves + (threadIdx.x >> 6));
+  if (t >= N) return;
+  const int lane = threadIdx.x & 63;
+  const int myslot = load_slot(slot_of, t, K, lane, cap);
+  quant_row_fp8<NI>(x + (int64_t)t * (H >> 3), recv_q, recv_scales, myslot, K, H, lane);
   write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+}
+
+// ---------------------------------------------------------------- low latency
+// One launch moves a decode-sized batch: routing and payload together.
+// Expert e owns R sub-blocks of M rows, one per source rank; pair (t, k) of
+// source s routed to e goes to slot (e*R + s)*M + j, j being its rank among
+// source s's pairs routed to e in (token, k) order.  A slot therefore depends
+// only on the pairs of its own source, and no device-wide scan is needed.
+// Block (s, q) ranks all pairs of source s (redundantly with the source's
+// other blocks; T*K <= kAssignTile) and then moves the rows of its own
+// kLLWaves tokens, one wavefront per token.  Pairs beyond M in a sub-block
+// get no slot and set EP_LAYOUT_ERR_OVERFLOW in the source's flags.
+constexpr int kLLThreads = 256;
+constexpr int kLLWaves = kLLThreads / 64;
+
+template <bool FP8, int NV>
+__global__ __launch_bounds__(kLLThreads) void ll_dispatch_kernel(
+    const int32_t* __restrict__ topk_idx, const u32x4* __restrict__ x,
+    const float* __restrict__ w, int32_t* __restrict__ recv_count, int32_t* __restrict__ slot_of,
+    int32_t* __restrict__ flags, u32x4* __restrict__ recv_x, float* __restrict__ recv_scales,
+    int32_t* __restrict__ recv_src, float* __restrict__ recv_w, int K, int E, int R, int T,
+    int M, int H, int Q) {
+  __shared__ int sidx[kAssignTile];
+  __shared__ int sslot[kAssignTile];
+  __shared__ int cnt[EP_MAX_EXPERTS];
+  __shared__ int ferr;
+  extern __shared__ unsigned long long masks[];  // [kLLWaves][E]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int s = blockIdx.x / Q, q = blockIdx.x % Q;
+  const int np = T * K;
+  const int64_t p0 = (int64_t)s * T * K;
+  int iv[kAssignTile / kLLThreads];
+  load_idx<kLLThreads, kAssignTile>(iv, topk_idx + p0, np);
+  for (int e = tid; e < E; e += kLLThreads) {
+    cnt[e] = 0;
+#pragma unroll
+    for (int ww = 0; ww < kLLWaves; ww++) masks[ww * E + e] = 0ull;
+  }
+  if (tid == 0) ferr = 0;
+  __syncthreads();
+  store_idx<kLLThreads, kAssignTile>(sidx, iv, np);
+  __syncthreads();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int myerr = 0;
+  for (int r0 = 0; r0 < np; r0 += kLLThreads) {
+    const int p = r0 + tid;
+    const int e = (p < np) ? sidx[p] : -1;
+    const bool ok = (e >= 0 && e < E);
+    if (p < np && !ok && e != -1) myerr |= EP_LAYOUT_ERR_INDEX;
+    if (ok) atomicOr(&masks[wv * E + e], 1ull << lane);
+    __syncthreads();
+    int slot = -1;
+    unsigned long long m = 0;
+    if (ok) {
+      m = masks[wv * E + e];
+      int pw = 0;
+      for (int w2 = 0; w2 < wv; w2++) pw += __popcll(masks[w2 * E + e]);
+      const int j = cnt[e] + pw + __popcll(m & below);
+      if (j < M) slot = (e * R + s) * M + j;
+      else myerr |= EP_LAYOUT_ERR_OVERFLOW;
+    }
+    __syncthreads();
+    if (ok && (m & below) == 0ull) {
+      atomicAdd(&cnt[e], __popcll(m));
+      masks[wv * E + e] = 0ull;
+    }
+    if (p < np) sslot[p] = slot;
+    __syncthreads();
+  }
+  if (myerr) atomicOr(&ferr, myerr);
+  __syncthreads();
+  if (q == 0) {
+    for (int e = tid; e < E; e += kLLThreads) recv_count[(int64_t)e * R + s] = min(cnt[e], M);
+    if (tid == 0) flags[s] = ferr;
+  }
+  const int per = (T + Q - 1) / Q;
+  const int ta = q * per, tb = min(T, ta + per);
+  for (int i = ta * K + tid; i < tb * K; i += kLLThreads) slot_of[p0 + i] = sslot[i];
+  for (int tl = ta + wv; tl < tb; tl += kLLWaves) {
+    const int t = uniform(s * T + tl);
+    const int myslot = (lane < K) ? sslot[tl * K + lane] : -1;
+    if constexpr (FP8)
+      quant_row_fp8<NV>(x + (int64_t)t * (H >> 3), recv_x, recv_scales, myslot, K, H, lane);
+    else
+      copy_row_bf16<64, NV>(x + (int64_t)t * (H >> 3), recv_x, myslot, K, H >> 3, lane);
+    write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+  }
+}
+
+// N == 0 in the low-latency path: zero counts and flags.
+__global__ __launch_bounds__(kThreads) void ll_empty_kernel(int32_t* __restrict__ recv_count,
+                                                             int32_t* __restrict__ flags, int E,
+                                                             int R) {
+  for (int q = threadIdx.x; q < E * R; q += kThreads) recv_count[q] = 0;
+  for (int q = threadIdx.x; q < R; q += kThreads) flags[q] = 0;
 }
 
 // ---------------------------------------------------------------- combine
@@ -1093,6 +1193,16 @@ void launch_combine(int q, int N, hipStream_t st, const void* eo, const int32_t*
 #undef EP_CQ
 }
 
+template <bool FP8, int NV>
+void launch_ll(int grid, size_t lds, hipStream_t st, const int32_t* idx, const void* x,
+               const float* w, int32_t* recv_count, int32_t* slot_of, int32_t* flags,
+               void* recv_x, float* recv_scales, int32_t* recv_src, float* recv_w, int K, int E,
+               int R, int T, int M, int H, int Q) {
+  ll_dispatch_kernel<FP8, NV><<<grid, kLLThreads, lds, st>>>(
+      idx, (const u32x4*)x, w, recv_count, slot_of, flags, (u32x4*)recv_x, recv_scales, recv_src,
+      recv_w, K, E, R, T, M, H, Q);
+}
+
 }  // namespace
 
 // ===================================================================== C ABI
@@ -1239,6 +1349,63 @@ int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slo
          (long long)recv_capacity, q > 16 ? 16 : (q == 3 ? 4 : q), q > 16 ? " (multi-pass)" : "");
   launch_combine(q, N, st, expert_out, slot_of, topk_weights, y, p->num_topk, H8, recv_capacity);
   return check_launch("combine");
+}
+
+int64_t ep_ll_capacity(const ep_problem_t* p, int32_t max_tokens_per_rank) {
+  if (validate_layout(p) != EP_OK || max_tokens_per_rank < 1) return -1;
+  const int64_t cap = (int64_t)p->num_experts * p->num_ranks * max_tokens_per_rank;
+  return cap > INT32_MAX ? -1 : cap;
+}
+
+int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const int32_t* topk_idx,
+                   const void* x, const float* topk_weights, int32_t* recv_count,
+                   int32_t* slot_of, int32_t* flags, void* recv_x, float* recv_scales,
+                   int32_t* recv_src_idx, float* recv_topk_weights, void* stream) {
+  int rc = validate_payload(p);
+  if (rc != EP_OK) return rc;
+  const int N = p->num_tokens, K = p->num_topk, E = p->num_experts, R = p->num_ranks;
+  const int M = max_tokens_per_rank, H = p->hidden;
+  if (ep_ll_capacity(p, M) < 0) return EP_ERR_INVALID_ARG;
+  const int T = N / R;
+  if ((int64_t)T * K > kAssignTile) return EP_ERR_INVALID_ARG;
+  if (!recv_count || !flags) return EP_ERR_INVALID_ARG;
+  if (N > 0 && (!topk_idx || !x || !slot_of || !recv_x)) return EP_ERR_INVALID_ARG;
+  if (p->use_fp8 && N > 0 && !recv_scales) return EP_ERR_INVALID_ARG;
+  if (recv_topk_weights && N > 0 && !topk_weights) return EP_ERR_INVALID_ARG;
+  rc = check_device();
+  if (rc != EP_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (N == 0) {
+    ll_empty_kernel<<<1, kThreads, 0, st>>>(recv_count, flags, E, R);
+    return check_launch("ll_empty");
+  }
+  const int Q = (T + kLLWaves - 1) / kLLWaves;
+  const int grid = R * Q;
+  const size_t lds = sizeof(unsigned long long) * kLLWaves * (size_t)E;
+  EP_LOG("ll dispatch N=%d H=%d K=%d E=%d R=%d M=%d fp8=%d: blocks=%d", N, H, K, E, R, M,
+         p->use_fp8, grid);
+#define EP_LL(FP, NV)                                                                        \
+  launch_ll<FP, NV>(grid, lds, st, topk_idx, x, topk_weights, recv_count, slot_of, flags,   \
+                    recv_x, recv_scales, recv_src_idx, recv_topk_weights, K, E, R, T, M, H, Q)
+  if (!p->use_fp8) {
+    const int q = (H / 8 + 63) / 64;
+    if (q <= 1) EP_LL(false, 1);
+    else if (q <= 2) EP_LL(false, 2);
+    else if (q <= 4) EP_LL(false, 4);
+    else if (q <= 7) EP_LL(false, 7);
+    else if (q <= 8) EP_LL(false, 8);
+    else if (q <= 14) EP_LL(false, 14);
+    else EP_LL(false, 16);
+  } else {
+    const int q = (H + 1023) / 1024;
+    if (q <= 1) EP_LL(true, 1);
+    else if (q <= 2) EP_LL(true, 2);
+    else if (q <= 4) EP_LL(true, 4);
+    else if (q <= 7) EP_LL(true, 7);
+    else EP_LL(true, 8);
+  }
+#undef EP_LL
+  return check_launch("ll_dispatch");
 }
 
 int ep_layout_error(const void* workspace, int32_t* flags, void* stream) {

@@ -65,8 +65,10 @@ enum {
 #define EP_MAX_RANKS 256
 #define EP_MAX_TOPK 32
 
-/* Bits of the device error word read by ep_layout_error. */
-#define EP_LAYOUT_ERR_INDEX 1 /* some topk_idx entry was outside [-1, E) */
+/* Bits of the device error word read by ep_layout_error, and of the
+ * per-source flags of ep_ll_dispatch. */
+#define EP_LAYOUT_ERR_INDEX 1    /* some topk_idx entry was outside [-1, E)        */
+#define EP_LAYOUT_ERR_OVERFLOW 2 /* ep_ll_dispatch: a sub-block had more than M pairs */
 
 /* Problem descriptor (host memory, read during the call only).
  *   num_tokens        N >= 0, all virtual source ranks together, N % R == 0
@@ -97,9 +99,10 @@ typedef struct ep_problem {
 int64_t ep_recv_capacity(const ep_problem_t* p);
 
 /* Bytes of device workspace ep_get_layout needs for this descriptor (host
- * only; -1 if invalid).  The workspace holds per-block histograms, their
- * prefix sums and the error word.  It needs no initialisation, and its
- * contents stay meaningful for ep_layout_error until the next layout call. */
+ * only; -1 if invalid).  The workspace holds the error word and, for problems
+ * laid out in two launches, per-block expert histograms, rank counts and
+ * error flags.  It needs no initialisation, and its error word stays
+ * meaningful for ep_layout_error until the next layout call. */
 int64_t ep_workspace_bytes(const ep_problem_t* p);
 
 /* Routing layout (DeepEP book ch.1 sec. 1.4 names the first three outputs).
@@ -163,6 +166,35 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
  * Does not read use_fp8: expert outputs are bf16 in both modes. */
 int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slot_of,
                const float* topk_weights, void* y, int64_t recv_capacity, void* stream);
+
+/* Low-latency dispatch: routing and payload in ONE launch, for decode-sized
+ * batches (DeepEP's second kernel family: lesson 14 sec. 3 shows
+ * low_latency_dispatch(x, topk_idx, topk_weights,
+ * num_max_dispatch_tokens_per_rank) feeding a masked grouped GEMM; the
+ * hotdry analysis, section "two kernel families", places it at decode batches
+ * of at most a few hundred tokens per rank).
+ * Layout: expert e owns R sub-blocks of M = max_tokens_per_rank rows, one per
+ * source rank, [E][R][M][H].  Pair (t, k) of source s routed to expert e goes
+ * to slot (e*R + s)*M + j, where j counts the earlier pairs of source s routed
+ * to e in (token, k) order.  A slot thus depends only on its own source's
+ * pairs: no device-wide scan, no workspace, deterministic.
+ *   max_tokens_per_rank  M >= 1; E*R*M <= INT32_MAX; (N/R)*K <= 4096
+ *   topk_idx, x, topk_weights  as for ep_get_layout / ep_dispatch
+ *   recv_count  [E][R] int32 out: rows used in sub-block (e, s) (<= M); the
+ *               mask of the masked GEMM
+ *   slot_of     [N][K] int32 out: the handle for ep_combine (with
+ *               recv_capacity = ep_ll_capacity), -1 = no slot
+ *   flags       [R] int32 out: per-source EP_LAYOUT_ERR_* bits; a pair beyond
+ *               M in its sub-block gets no slot and sets ..._OVERFLOW
+ *   recv_x, recv_scales, recv_src_idx, recv_topk_weights: as for ep_dispatch,
+ *               with ep_ll_capacity rows; only rows holding a pair are
+ *               written (rows j >= recv_count of a sub-block keep old bytes)
+ * Ignores expert_alignment. */
+int64_t ep_ll_capacity(const ep_problem_t* p, int32_t max_tokens_per_rank);
+int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const int32_t* topk_idx,
+                   const void* x, const float* topk_weights, int32_t* recv_count,
+                   int32_t* slot_of, int32_t* flags, void* recv_x, float* recv_scales,
+                   int32_t* recv_src_idx, float* recv_topk_weights, void* stream);
 
 /* SYNCHRONOUS debug query: waits for `stream`, then stores the error word of
  * the last ep_get_layout that used `workspace` into *flags (host pointer).

@@ -55,6 +55,8 @@ def load(path):
     L.oracle_layout.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32p,
                                 _i32p, _i32p, _u8p, _i32p, _i32p, _i32p]
     L.oracle_recv_meta.argtypes = [_i32, _i32, _i64, _i32p, _f32p, _i32p, _f32p]
+    L.oracle_ll_layout.restype = ctypes.c_int
+    L.oracle_ll_layout.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p]
     L.oracle_dispatch_bf16.argtypes = [_i32, _i32, _i32, _u16p, _i32p, _u16p]
     L.oracle_quantize_row.argtypes = [_i32, _u16p, _u8p, _f32p]
     L.oracle_dispatch_fp8.argtypes = [_i32, _i32, _i32, _u16p, _i32p, _u8p, _f32p]
@@ -142,6 +144,23 @@ def layout(topk_idx, num_experts, num_ranks, expert_alignment=1):
                              out["slot_of"].reshape(-1) if N else np.zeros(1, np.int32))
     if rc < 0:
         raise ValueError("oracle_layout: invalid sizes")
+    out["error_flags"] = rc
+    return out
+
+
+def ll_layout(topk_idx, num_experts, num_ranks, max_tokens_per_rank):
+    """Low-latency layout: dict(recv_count [E, R], slot_of [N, K], flags [R])."""
+    topk_idx = _c(topk_idx, np.int32)
+    N, K = topk_idx.shape
+    E, R, M = int(num_experts), int(num_ranks), int(max_tokens_per_rank)
+    out = dict(recv_count=np.zeros((E, R), np.int32), slot_of=np.zeros((N, K), np.int32),
+               flags=np.zeros(R, np.int32))
+    rc = lib().oracle_ll_layout(N, K, E, R, M, topk_idx.reshape(-1) if N else np.zeros(1, np.int32),
+                                out["recv_count"].reshape(-1),
+                                out["slot_of"].reshape(-1) if N else np.zeros(1, np.int32),
+                                out["flags"])
+    if rc < 0:
+        raise ValueError("oracle_ll_layout: invalid sizes")
     out["error_flags"] = rc
     return out
 

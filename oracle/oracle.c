@@ -221,6 +221,54 @@ void oracle_recv_meta(int32_t N, int32_t K, int64_t cap, const int32_t* slot_of,
     }
 }
 
+/* Low-latency layout: every expert e owns R sub-blocks of M rows, one per
+ * source rank, so slot (e*R + s)*M + j holds the j-th pair of source s routed
+ * to e, counting in token order then k order (the lesson-14 queue order,
+ * restricted to one source).  Pairs beyond M in a sub-block get no slot and
+ * set bit 1 of the source's flags; indices outside [-1, E) set bit 0.
+ *   recv_count[e][s]  rows used in sub-block (e, s)  (at most M)
+ *   slot_of[t][k]     slot of pair (t, k), -1 when it has none
+ *   flags[s]          error bits of source s
+ * The capacity is E*R*M slots.  Returns -1 for bad sizes, else the OR of the
+ * flags. */
+int oracle_ll_layout(int32_t N, int32_t K, int32_t E, int32_t R, int32_t M,
+                     const int32_t* topk_idx, int32_t* recv_count, int32_t* slot_of,
+                     int32_t* flags) {
+  if (N < 0 || K < 1 || E < 1 || R < 1 || M < 1) return -1;
+  if (E % R != 0 || N % R != 0) return -1;
+  int32_t T = N / R;
+  int all = 0;
+  int32_t* cnt = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  if (!cnt) return -1;
+  for (int32_t s = 0; s < R; s++) {
+    int f = 0;
+    for (int32_t e = 0; e < E; e++) cnt[e] = 0;
+    for (int32_t t = s * T; t < (s + 1) * T; t++) {
+      for (int32_t k = 0; k < K; k++) {
+        int32_t e = topk_idx[(int64_t)t * K + k];
+        int64_t q = (int64_t)t * K + k;
+        slot_of[q] = -1;
+        if (e == -1) continue;
+        if (e < -1 || e >= E) {
+          f |= 1;
+          continue;
+        }
+        if (cnt[e] >= M) {
+          f |= 2;
+          continue;
+        }
+        slot_of[q] = ((e * R) + s) * M + cnt[e];
+        cnt[e] += 1;
+      }
+    }
+    for (int32_t e = 0; e < E; e++) recv_count[(int64_t)e * R + s] = cnt[e];
+    flags[s] = f;
+    all |= f;
+  }
+  free(cnt);
+  return all;
+}
+
 /* ------------------------------------------------------------------ */
 /* dispatch                                                            */
 /* ------------------------------------------------------------------ */

@@ -112,3 +112,24 @@ def test_payload_rejects_bad_descriptors():
     assert L.ep_get_layout(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake,
                            ctypes.c_void_p(260), None) == 1
     assert L.ep_layout_error(None, None, None) == 1
+
+
+def test_ll_capacity_and_validation():
+    L = ep.lib()
+    assert ep.ll_capacity(1024, 8, 256, 8, 128) == 256 * 8 * 128
+    with pytest.raises(ValueError):
+        ep.ll_capacity(1024, 8, 256, 8, 0)                # M >= 1
+    with pytest.raises(ValueError):
+        ep.ll_capacity(1024, 8, 1024, 256, 1 << 20)       # E*R*M beyond int32
+    fake = ctypes.c_void_p(256)
+    args = [fake] * 10 + [None]
+    # (N/R)*K above 4096 pairs per source
+    p = _p(num_tokens=8 * 1024, num_topk=8, num_experts=16, num_ranks=8)
+    assert L.ep_ll_dispatch(ctypes.byref(p), 1024, *args) == 1
+    # fp8 needs hidden % 128 and a scale buffer
+    p = _p(hidden=136, use_fp8=True)
+    assert L.ep_ll_dispatch(ctypes.byref(p), 8, *args) == 1
+    p = _p(use_fp8=True)
+    a = list(args)
+    a[7] = None
+    assert L.ep_ll_dispatch(ctypes.byref(p), 8, *a) == 1

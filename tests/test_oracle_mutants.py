@@ -16,6 +16,7 @@ from oracle import build as obuild
 from . import test_oracle_dispatch_combine as tdc
 from . import test_oracle_formats as tf
 from . import test_oracle_layout as tl
+from . import test_oracle_ll as tll
 
 MUTANTS = {
     # layout: k walked backwards -> duplicate experts in a row get swapped slots
@@ -47,6 +48,13 @@ MUTANTS = {
     "fp8_scale": ("float scale = amax / 448.0f;", "float scale = amax / 480.0f;"),
     # quantiser: group stride wrong (first element of each group missed)
     "fp8_amax": ("for (int32_t i = 0; i < 128; i++) {\n      float a = fabsf", "for (int32_t i = 1; i < 128; i++) {\n      float a = fabsf"),
+    # low-latency layout: counters not reset per source
+    "ll_reset": ("    for (int32_t e = 0; e < E; e++) cnt[e] = 0;\n    for (int32_t t = s * T;",
+                 "    for (int32_t t = s * T;"),
+    # low-latency layout: source-major instead of expert-major sub-blocks
+    "ll_slot": ("slot_of[q] = ((e * R) + s) * M + cnt[e];", "slot_of[q] = ((s * E) + e) * M + cnt[e];"),
+    # low-latency layout: overflow check off by one
+    "ll_overflow": ("if (cnt[e] >= M) {", "if (cnt[e] > M) {"),
     # fp8 dispatch: scales copied to the wrong row
     "fp8_copy": ("memcpy(recv_scales + (int64_t)s * G, sc", "memcpy(recv_scales + (int64_t)t * G, sc"),
 }
@@ -70,6 +78,11 @@ def _pins(orc):
     for w in tdc.CASES[:2]:
         yield f"ident_{w.name}", (lambda w=w: tdc.test_identity_round_trip_bf16(orc, w))
     yield "fp8_rt", lambda: tdc.test_fp8_dispatch_and_identity_round_trip(orc)
+    yield "ll_golden", lambda: tll.test_ll_golden(orc)
+    for trial in range(30):
+        yield f"ll_brute{trial}", (lambda tr=trial: tll.test_ll_bruteforce(orc, tr))
+    for trial in range(3):
+        yield f"ll_compact{trial}", (lambda tr=trial: tll.test_ll_agrees_with_compact_layout(orc, tr))
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
