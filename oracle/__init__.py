@@ -55,6 +55,9 @@ def load(path):
     L.oracle_layout.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32p,
                                 _i32p, _i32p, _u8p, _i32p, _i32p, _i32p]
     L.oracle_recv_meta.argtypes = [_i32, _i32, _i64, _i32p, _f32p, _i32p, _f32p]
+    L.oracle_dispatch_quantized.argtypes = [_i32, _i32, _i32, _u8p, _f32p, _i32p, _u8p, _f32p]
+    L.oracle_zero_padding.argtypes = [_i32, _i32, _i32, _i32p, _i32p, _u8p, _vp]
+    L.oracle_accumulate_stats.argtypes = [_i32, _i32p, np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")]
     L.oracle_ll_layout.restype = ctypes.c_int
     L.oracle_ll_layout.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p]
     L.oracle_dispatch_bf16.argtypes = [_i32, _i32, _i32, _u16p, _i32p, _u16p]
@@ -214,6 +217,38 @@ def dispatch_fp8(x_bits, slot_of, cap):
         lib().oracle_dispatch_fp8(N, K, H, x_bits.reshape(-1), slot_of.reshape(-1),
                                   q.reshape(-1), sc.reshape(-1))
     return q, sc
+
+
+def dispatch_quantized(codes, scales, slot_of, cap):
+    """Copy given e4m3 codes [N, H] and scales [N, H/128] to every slot."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    slot_of = _c(slot_of, np.int32)
+    N, H = codes.shape
+    K = slot_of.shape[1]
+    q = np.zeros((cap, H), np.uint8)
+    sc = np.zeros((cap, H // 128), np.float32)
+    if N and cap:
+        lib().oracle_dispatch_quantized(N, K, H, codes.reshape(-1), scales.reshape(-1),
+                                        slot_of.reshape(-1), q.reshape(-1), sc.reshape(-1))
+    return q, sc
+
+
+def zero_padding(recv_x, recv_scales, expert_slot_offset, num_recv_per_expert):
+    """In place: zero the padding rows (and scale rows) of every expert region."""
+    assert recv_x.flags["C_CONTIGUOUS"]
+    E = int(num_recv_per_expert.size)
+    row_bytes = recv_x.shape[1] * recv_x.itemsize
+    raw = recv_x.reshape(-1).view(np.uint8)
+    G = 0 if recv_scales is None else recv_scales.shape[1]
+    lib().oracle_zero_padding(E, row_bytes, G, _c(expert_slot_offset, np.int32),
+                              _c(num_recv_per_expert, np.int32), raw,
+                              None if recv_scales is None else recv_scales.ctypes.data)
+
+
+def accumulate_stats(count, stats):
+    """In place: stats[e] += count[e] (stats int64)."""
+    lib().oracle_accumulate_stats(int(count.size), _c(count, np.int32), stats)
 
 
 # ---------------------------------------------------------------- combine

@@ -340,6 +340,40 @@ void oracle_dispatch_fp8(int32_t N, int32_t K, int32_t H, const uint16_t* x,
   free(sc);
 }
 
+/* Pre-quantised payload (DeepEP's dispatch also takes x as a pair of codes
+ * and scales, DeepEP book ch.1 sec. 1.1 and 1.4): the given codes [N][H] and
+ * scales [N][H/128] are copied unchanged to every slot of their token. */
+void oracle_dispatch_quantized(int32_t N, int32_t K, int32_t H, const uint8_t* codes,
+                               const float* scales, const int32_t* slot_of, uint8_t* recv_q,
+                               float* recv_scales) {
+  int32_t G = H / 128;
+  for (int32_t t = 0; t < N; t++)
+    for (int32_t k = 0; k < K; k++) {
+      int32_t s = slot_of[(int64_t)t * K + k];
+      if (s < 0) continue;
+      memcpy(recv_q + (int64_t)s * H, codes + (int64_t)t * H, (size_t)H);
+      memcpy(recv_scales + (int64_t)s * G, scales + (int64_t)t * G, sizeof(float) * (size_t)G);
+    }
+}
+
+/* Zero padding (DeepEP's do_zero_padding): the padding rows of every expert
+ * region, slots [off[e] + count[e], off[e+1]), are set to zero bytes; so are
+ * their scale rows when scales != NULL.  row_bytes is 2H (bf16) or H (e4m3). */
+void oracle_zero_padding(int32_t E, int32_t row_bytes, int32_t G, const int32_t* off,
+                         const int32_t* count, uint8_t* recv_x, float* recv_scales) {
+  for (int32_t e = 0; e < E; e++)
+    for (int64_t s = (int64_t)off[e] + count[e]; s < off[e + 1]; s++) {
+      memset(recv_x + s * row_bytes, 0, (size_t)row_bytes);
+      if (recv_scales) memset(recv_scales + s * G, 0, sizeof(float) * (size_t)G);
+    }
+}
+
+/* Running per-expert receive statistics (DeepEP's
+ * cumulative_local_expert_recv_stats, book ch.1 sec. 1.1): stats[e] += count[e]. */
+void oracle_accumulate_stats(int32_t E, const int32_t* count, int64_t* stats) {
+  for (int32_t e = 0; e < E; e++) stats[e] += count[e];
+}
+
 /* ------------------------------------------------------------------ */
 /* combine                                                             */
 /* ------------------------------------------------------------------ */

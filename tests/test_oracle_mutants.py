@@ -17,6 +17,7 @@ from . import test_oracle_dispatch_combine as tdc
 from . import test_oracle_formats as tf
 from . import test_oracle_layout as tl
 from . import test_oracle_ll as tll
+from . import test_oracle_variants as tv
 
 MUTANTS = {
     # layout: k walked backwards -> duplicate experts in a row get swapped slots
@@ -57,6 +58,14 @@ MUTANTS = {
     "ll_overflow": ("if (cnt[e] >= M) {", "if (cnt[e] > M) {"),
     # fp8 dispatch: scales copied to the wrong row
     "fp8_copy": ("memcpy(recv_scales + (int64_t)s * G, sc", "memcpy(recv_scales + (int64_t)t * G, sc"),
+    # pre-quantised pass-through: scales taken from the wrong token row
+    "q_scales": ("memcpy(recv_scales + (int64_t)s * G, scales + (int64_t)t * G",
+                 "memcpy(recv_scales + (int64_t)s * G, scales + (int64_t)k * G"),
+    # zero padding: the whole region cleared instead of its tail
+    "zp_start": ("for (int64_t s = (int64_t)off[e] + count[e]; s < off[e + 1]; s++)",
+                 "for (int64_t s = (int64_t)off[e]; s < off[e + 1]; s++)"),
+    # running statistics overwritten instead of accumulated
+    "stats": ("stats[e] += count[e];", "stats[e] = count[e];"),
 }
 
 
@@ -83,6 +92,10 @@ def _pins(orc):
         yield f"ll_brute{trial}", (lambda tr=trial: tll.test_ll_bruteforce(orc, tr))
     for trial in range(3):
         yield f"ll_compact{trial}", (lambda tr=trial: tll.test_ll_agrees_with_compact_layout(orc, tr))
+    for w in tv.CASES:
+        yield f"q_brute_{w.name}", (lambda w=w: tv.test_prequantized_passthrough_bruteforce(orc, w))
+        yield f"zp_{w.name}", (lambda w=w: tv.test_zero_padding_bruteforce(orc, w, True))
+        yield f"stats_{w.name}", (lambda w=w: tv.test_cumulative_stats_are_a_histogram(orc, w))
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
