@@ -31,7 +31,20 @@ class Problem(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("num_topk", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("num_ranks", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
-                ("use_fp8", ctypes.c_int32)]
+                ("use_fp8", ctypes.c_int32), ("topk_idx_bytes", ctypes.c_int32)]
+
+
+EP_DISPATCH_ZERO_PADDING = 1
+
+
+class DispatchArgs(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("x_scales", ctypes.c_void_p),
+                ("topk_weights", ctypes.c_void_p), ("slot_of", ctypes.c_void_p),
+                ("expert_slot_offset", ctypes.c_void_p), ("num_recv_per_expert", ctypes.c_void_p),
+                ("recv_x", ctypes.c_void_p), ("recv_scales", ctypes.c_void_p),
+                ("recv_src_idx", ctypes.c_void_p), ("recv_topk_weights", ctypes.c_void_p),
+                ("recv_capacity", ctypes.c_int64), ("cumulative_recv_stats", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32)]
 
 
 class EPError(RuntimeError):
@@ -42,7 +55,8 @@ class EPError(RuntimeError):
 
 
 EXPORTS = ("ep_recv_capacity", "ep_workspace_bytes", "ep_get_layout", "ep_dispatch",
-           "ep_combine", "ep_layout_error", "ep_status_str", "ep_ll_capacity", "ep_ll_dispatch")
+           "ep_dispatch_ex", "ep_combine", "ep_layout_error", "ep_status_str", "ep_ll_capacity",
+           "ep_ll_dispatch")
 EP_LAYOUT_ERR_OVERFLOW = 2
 
 
@@ -77,6 +91,8 @@ def load(path):
     L.ep_get_layout.argtypes = [P] + [vp] * 9
     L.ep_dispatch.restype = ctypes.c_int
     L.ep_dispatch.argtypes = [P] + [vp] * 9 + [i64, vp]
+    L.ep_dispatch_ex.restype = ctypes.c_int
+    L.ep_dispatch_ex.argtypes = [P, ctypes.POINTER(DispatchArgs), vp]
     L.ep_combine.restype = ctypes.c_int
     L.ep_combine.argtypes = [P, vp, vp, vp, vp, i64, vp]
     L.ep_layout_error.restype = ctypes.c_int
@@ -91,9 +107,19 @@ def load(path):
 
 
 def problem(num_tokens, hidden, num_topk, num_experts, num_ranks, expert_alignment=1,
-            use_fp8=False):
+            use_fp8=False, topk_idx_bytes=4):
     return Problem(int(num_tokens), int(hidden), int(num_topk), int(num_experts),
-                   int(num_ranks), int(expert_alignment), int(bool(use_fp8)))
+                   int(num_ranks), int(expert_alignment), int(bool(use_fp8)),
+                   int(topk_idx_bytes))
+
+
+def _idx_bytes(topk_idx):
+    import torch
+    if topk_idx.dtype == torch.int32:
+        return 4
+    if topk_idx.dtype == torch.int64:
+        return 8
+    raise ValueError(f"topk_idx: need int32 or int64, got {topk_idx.dtype}")
 
 
 def recv_capacity(num_tokens, num_topk, num_experts, num_ranks, expert_alignment=1):
@@ -177,7 +203,7 @@ def alloc_layout(num_tokens, num_topk, num_experts, num_ranks, expert_alignment=
 
 
 def get_layout(topk_idx, num_experts, num_ranks, expert_alignment=1, out=None):
-    """Routing layout of ``topk_idx`` [N, K] int32 (see ep_get_layout)."""
+    """Routing layout of ``topk_idx`` [N, K] int32 or int64 (see ep_get_layout)."""
     import torch
     N, K = topk_idx.shape
     if out is None:
@@ -185,8 +211,10 @@ def get_layout(topk_idx, num_experts, num_ranks, expert_alignment=1, out=None):
     if (out.num_experts, out.num_ranks, out.expert_alignment) != \
             (num_experts, num_ranks, expert_alignment):
         raise ValueError("get_layout: `out` was allocated for another problem")
-    _need(topk_idx, torch.int32, (out.num_tokens, out.num_topk), "topk_idx")
+    nb = _idx_bytes(topk_idx)
+    _need(topk_idx, topk_idx.dtype, (out.num_tokens, out.num_topk), "topk_idx")
     p = out.problem()
+    p.topk_idx_bytes = nb
     rc = lib().ep_get_layout(ctypes.byref(p), _ptr(topk_idx), _ptr(out.num_tokens_per_rank),
                              _ptr(out.num_tokens_per_expert), _ptr(out.is_token_in_rank),
                              _ptr(out.num_recv_per_expert), _ptr(out.expert_slot_offset),
@@ -208,16 +236,29 @@ def alloc_recv(layout, hidden, use_fp8=False, device="cuda", capacity=None):
             torch.empty((cap,), dtype=torch.float32, device=device))
 
 
-def dispatch(x, topk_weights, layout, use_fp8=False, out=None, with_meta=True):
-    """Scatter ``x`` [N, H] bf16 into expert-contiguous receive slots.
+def dispatch(x, topk_weights, layout, use_fp8=False, out=None, with_meta=True,
+             x_scales=None, zero_padding=False, cumulative_stats=None):
+    """Scatter ``x`` [N, H] into expert-contiguous receive slots.
 
     Returns (recv_x, recv_scales, recv_src_idx, recv_topk_weights); recv_x is
     bf16 or float8_e4m3fn [cap, H]; recv_scales is [cap, H/128] fp32 or None.
-    With ``with_meta=False`` the per-slot source/weight tags are skipped.
+    ``x`` is bf16, or, with ``x_scales`` [N, H/128] fp32 given, pre-quantised
+    float8_e4m3fn codes that are copied unchanged (needs use_fp8).
+    With ``with_meta=False`` the per-slot source/weight tags are skipped;
+    ``zero_padding`` zeroes the padding rows of every expert region;
+    ``cumulative_stats`` ([E] int64) gets the per-expert receive counts added.
     """
     import torch
     N, H = x.shape
-    _need(x, torch.bfloat16, (layout.num_tokens, H), "x")
+    if x_scales is not None:
+        if not use_fp8:
+            raise ValueError("dispatch: pre-quantised x needs use_fp8=True")
+        _need(x, torch.float8_e4m3fn, (layout.num_tokens, H), "x")
+        _need(x_scales, torch.float32, (layout.num_tokens, H // 128), "x_scales")
+    else:
+        _need(x, torch.bfloat16, (layout.num_tokens, H), "x")
+    if cumulative_stats is not None:
+        _need(cumulative_stats, torch.int64, (layout.num_experts,), "cumulative_stats")
     if out is None:
         out = alloc_recv(layout, H, use_fp8, x.device)
     recv_x, scales, src, rw = out
@@ -230,13 +271,31 @@ def dispatch(x, topk_weights, layout, use_fp8=False, out=None, with_meta=True):
         _need(rw, torch.float32, (cap,), "recv_topk_weights")
         _need(topk_weights, torch.float32, (layout.num_tokens, layout.num_topk), "topk_weights")
     p = layout.problem(H, use_fp8)
-    rc = lib().ep_dispatch(ctypes.byref(p), _ptr(x), _ptr(topk_weights if with_meta else None),
-                           _ptr(layout.slot_of), _ptr(layout.expert_slot_offset),
-                           _ptr(layout.num_recv_per_expert), _ptr(recv_x),
-                           _ptr(scales if use_fp8 else None),
-                           _ptr(src if with_meta else None), _ptr(rw if with_meta else None),
-                           cap, _stream())
-    _check("ep_dispatch", rc)
+    a = DispatchArgs()
+    a.x = x.data_ptr()
+    a.x_scales = None if x_scales is None else x_scales.data_ptr()
+    a.topk_weights = topk_weights.data_ptr() if with_meta else None
+    a.slot_of = layout.slot_of.data_ptr()
+    a.expert_slot_offset = layout.expert_slot_offset.data_ptr()
+    a.num_recv_per_expert = layout.num_recv_per_expert.data_ptr()
+    a.recv_x = recv_x.data_ptr()
+    a.recv_scales = scales.data_ptr() if use_fp8 else None
+    a.recv_src_idx = src.data_ptr() if with_meta else None
+    a.recv_topk_weights = rw.data_ptr() if with_meta else None
+    a.recv_capacity = cap
+    a.cumulative_recv_stats = None if cumulative_stats is None else cumulative_stats.data_ptr()
+    a.flags = EP_DISPATCH_ZERO_PADDING if zero_padding else 0
+    if x_scales is None and not zero_padding and cumulative_stats is None:
+        rc = lib().ep_dispatch(ctypes.byref(p), _ptr(x), _ptr(topk_weights if with_meta else None),
+                               _ptr(layout.slot_of), _ptr(layout.expert_slot_offset),
+                               _ptr(layout.num_recv_per_expert), _ptr(recv_x),
+                               _ptr(scales if use_fp8 else None),
+                               _ptr(src if with_meta else None), _ptr(rw if with_meta else None),
+                               cap, _stream())
+        _check("ep_dispatch", rc)
+    else:
+        _check("ep_dispatch_ex", lib().ep_dispatch_ex(ctypes.byref(p), ctypes.byref(a),
+                                                      _stream()))
     return recv_x, (scales if use_fp8 else None), src, rw
 
 
@@ -323,7 +382,8 @@ def ll_dispatch(x, topk_idx, topk_weights, num_experts, num_ranks, max_tokens_pe
             lay.max_tokens_per_rank) != (N, K, num_experts, num_ranks, max_tokens_per_rank):
         raise ValueError("ll_dispatch: `out` was allocated for another problem")
     _need(x, torch.bfloat16, (N, H), "x")
-    _need(topk_idx, torch.int32, (N, K), "topk_idx")
+    nb = _idx_bytes(topk_idx)
+    _need(topk_idx, topk_idx.dtype, (N, K), "topk_idx")
     recv_x, scales, src, rw = recv
     _need(recv_x, torch.float8_e4m3fn if use_fp8 else torch.bfloat16, (lay.capacity, H), "recv_x")
     if use_fp8:
@@ -332,7 +392,7 @@ def ll_dispatch(x, topk_idx, topk_weights, num_experts, num_ranks, max_tokens_pe
         _need(src, torch.int32, (lay.capacity,), "recv_src_idx")
         _need(rw, torch.float32, (lay.capacity,), "recv_topk_weights")
         _need(topk_weights, torch.float32, (N, K), "topk_weights")
-    p = problem(N, H, K, num_experts, num_ranks, 1, use_fp8)
+    p = problem(N, H, K, num_experts, num_ranks, 1, use_fp8, nb)
     rc = lib().ep_ll_dispatch(ctypes.byref(p), int(max_tokens_per_rank), _ptr(topk_idx), _ptr(x),
                               _ptr(topk_weights if with_meta else None), _ptr(lay.recv_count),
                               _ptr(lay.slot_of), _ptr(lay.flags), _ptr(recv_x),

@@ -147,11 +147,19 @@ constexpr int kFlagBytes = 16384;       // LDS for is_token_in_rank staging
 // Load n (1 <= n <= TILE) consecutive pairs of topk_idx into registers without
 // branches (the index is clamped, so every lane issues its loads back to
 // back), then store them to sidx[0, n).
-template <int BLK, int TILE>
-__device__ __forceinline__ void load_idx(int (&v)[TILE / BLK], const int32_t* __restrict__ idx,
-                                         int n) {
+// Routing indices come as int32 or int64.  An int64 value that does not fit
+// in int32 becomes -2, which the kernels treat like every other value outside
+// [-1, E): skipped and flagged EP_LAYOUT_ERR_INDEX.
+__device__ __forceinline__ int to_expert(int32_t v) { return v; }
+__device__ __forceinline__ int to_expert(int64_t v) {
+  return (v >= -1 && v <= INT32_MAX) ? (int)v : -2;
+}
+
+template <int BLK, int TILE, typename I>
+__device__ __forceinline__ void load_idx(int (&v)[TILE / BLK], const I* __restrict__ idx, int n) {
 #pragma unroll
-  for (int j = 0; j < TILE / BLK; j++) v[j] = idx[min(j * BLK + (int)threadIdx.x, n - 1)];
+  for (int j = 0; j < TILE / BLK; j++)
+    v[j] = to_expert(idx[min(j * BLK + (int)threadIdx.x, n - 1)]);
 }
 
 template <int BLK, int TILE>
@@ -166,8 +174,9 @@ __device__ __forceinline__ void store_idx(int* __restrict__ sidx, const int (&v)
 
 // Phase 1: per-block expert histogram, is_token_in_rank rows and per-block
 // per-rank token counts.  LDS atomics only count (order does not matter).
+template <typename I>
 __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
-    const int32_t* __restrict__ topk_idx, uint8_t* __restrict__ in_rank,
+    const I* __restrict__ topk_idx, uint8_t* __restrict__ in_rank,
     int32_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_rank, int32_t* __restrict__ blk_err,
     int K, int E, int R, int L, int T, int CB, int C) {
   __shared__ int sidx[kCountTile];
@@ -254,8 +263,9 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
 constexpr int kAssignThreads = 1024;
 constexpr int kAssignWaves = kAssignThreads / 64;
 
+template <typename I>
 __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_cnt,
+    const I* __restrict__ topk_idx, const int32_t* __restrict__ blk_cnt,
     const int32_t* __restrict__ blk_rank, const int32_t* __restrict__ blk_err,
     int32_t* __restrict__ err_word, int32_t* __restrict__ num_tokens_per_rank,
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_recv,
@@ -432,8 +442,9 @@ constexpr int kFusedThreads = 1024;
 constexpr int kFusedMaxPairs = EP_FUSED_MAX_PAIRS;
 constexpr int kFusedMaxExperts = 512;
 
+template <typename I>
 __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
-    const int32_t* __restrict__ topk_idx, uint8_t* __restrict__ in_rank,
+    const I* __restrict__ topk_idx, uint8_t* __restrict__ in_rank,
     int32_t* __restrict__ err_word, int32_t* __restrict__ num_tokens_per_rank,
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_recv,
     int32_t* __restrict__ off, int32_t* __restrict__ slot_of, int N, int K, int E, int R, int L,
@@ -473,7 +484,7 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
   for (int pb = 0; pb < NK; pb += 16 * BLK) {
     int v[16];
 #pragma unroll
-    for (int u = 0; u < 16; u++) v[u] = topk_idx[min(pb + u * BLK + tid, NK - 1)];
+    for (int u = 0; u < 16; u++) v[u] = to_expert(topk_idx[min(pb + u * BLK + tid, NK - 1)]);
 #pragma unroll
     for (int u = 0; u < 16; u++) {
       const int p = pb + u * BLK + tid;
@@ -627,6 +638,59 @@ __device__ __forceinline__ void fill_padding(int fb, const int32_t* __restrict__
   }
 }
 
+// Work of a dispatch launch besides the token rows, done by the first blocks
+// of its grid so that it runs alongside them: padding tags (fill blocks),
+// zeroed padding rows (zero blocks, DeepEP's do_zero_padding) and the running
+// per-expert receive counts (one stats block, DeepEP's
+// cumulative_local_expert_recv_stats).
+struct DispatchAux {
+  const int32_t* off;   // [E+1] expert region offsets
+  const int32_t* cnt;   // [E] pairs per expert
+  int32_t* recv_src;    // tags, or NULL
+  float* recv_w;
+  u32x4* recv_x;        // zero padding: rows of row16 16-byte chunks
+  float* recv_scales;   // and G scales per row (e4m3 payload), or NULL
+  int64_t* stats;       // [E], or NULL
+  int64_t cap;
+  int E, A, row16, G;
+  int fill_blocks, zero_blocks, stat_blocks;
+  __host__ __device__ int blocks() const { return fill_blocks + zero_blocks + stat_blocks; }
+};
+
+// Zero blocks: wavefront v of the zero range takes padding row j = v % (A-1)
+// of expert e = v / (A-1), which exists iff j < off[e+1] - off[e] - cnt[e]
+// (an expert region has fewer than A padding rows).  Consecutive waves take
+// consecutive rows of one expert, so blocks past an expert's padding exit
+// at once.
+template <int BLK>
+__device__ __forceinline__ void zero_padding_rows(int zb, const DispatchAux& a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t v = (int64_t)zb * (BLK / 64) + (threadIdx.x >> 6);
+  const int e = (int)(v / (a.A - 1)), j = (int)(v % (a.A - 1));
+  if (e >= a.E) return;
+  const int64_t row = (int64_t)a.off[e] + a.cnt[e] + j;
+  if (row >= a.off[e + 1] || row >= a.cap) return;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  u32x4* dst = a.recv_x + row * a.row16;
+  for (int c = lane; c < a.row16; c += 64) st16(dst + c, z);
+  if (a.recv_scales)
+    for (int g = lane; g < a.G; g += 64) a.recv_scales[row * a.G + g] = 0.0f;
+}
+
+template <int BLK>
+__device__ __forceinline__ void dispatch_aux(int b, const DispatchAux& a, int* s_off, int* s_cnt) {
+  if (b < a.fill_blocks) {
+    fill_padding<BLK>(b, a.off, a.cnt, a.E, a.cap, a.recv_src, a.recv_w, s_off, s_cnt);
+    return;
+  }
+  b -= a.fill_blocks;
+  if (b < a.zero_blocks) {
+    zero_padding_rows<BLK>(b, a);
+    return;
+  }
+  for (int e = threadIdx.x; e < a.E; e += BLK) a.stats[e] += a.cnt[e];
+}
+
 // Slot of pair (t, lane) for lanes < K, -1 elsewhere or when out of range.
 __device__ __forceinline__ int load_slot(const int32_t* __restrict__ slot_of, int t, int K,
                                          int lane, int64_t cap) {
@@ -648,12 +712,12 @@ __device__ __forceinline__ void write_meta(int t, int K, int lane, int myslot,
   }
 }
 
-// Copy one bf16 row (H8 16-byte chunks) to the slots that lanes 0..K-1 of
-// `myslot` name (-1: none).  TPT threads share the row; `vl` is this thread's
+// Copy one row (H8 16-byte chunks: bf16 or e4m3 codes) to the slots that
+// lanes 0..K-1 of `myslot` name (-1: none).  TPT threads share the row; `vl` is this thread's
 // index among them.  The row is read once into VGPRs per pass of NV chunks per
 // thread and stored to every slot.
 template <int TPT, int NV>
-__device__ __forceinline__ void copy_row_bf16(const u32x4* __restrict__ row,
+__device__ __forceinline__ void copy_row(const u32x4* __restrict__ row,
                                               u32x4* __restrict__ recv_x, int myslot, int K,
                                               int H8, int vl) {
   for (int base = 0; base < H8; base += TPT * NV) {
@@ -682,24 +746,24 @@ __device__ __forceinline__ void copy_row_bf16(const u32x4* __restrict__ row,
 template <int TPT, int NV, int BLK>
 __global__ __launch_bounds__(BLK) void dispatch_bf16_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
-    const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
     u32x4* __restrict__ recv_x, int32_t* __restrict__ recv_src, float* __restrict__ recv_w,
-    int N, int K, int E, int H8, int64_t cap, int fill_blocks) {
+    int N, int K, int H8, int64_t cap, DispatchAux aux) {
   __shared__ int s_off[EP_MAX_EXPERTS + 1];
   __shared__ int s_cnt[EP_MAX_EXPERTS];
-  // the padding-tag blocks come first so that they run alongside the token
+  // the auxiliary blocks come first so that they run alongside the token
   // blocks instead of after them
-  if ((int)blockIdx.x < fill_blocks) {
-    fill_padding<BLK>(blockIdx.x, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
+  const int nb = aux.blocks();
+  if ((int)blockIdx.x < nb) {
+    dispatch_aux<BLK>(blockIdx.x, aux, s_off, s_cnt);
     return;
   }
   constexpr int kTok = BLK / TPT;
-  const int t = uniform(((int)blockIdx.x - fill_blocks) * kTok + (int)(threadIdx.x / TPT));
+  const int t = uniform(((int)blockIdx.x - nb) * kTok + (int)(threadIdx.x / TPT));
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
   const int vl = threadIdx.x % TPT;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
-  copy_row_bf16<TPT, NV>(x + (int64_t)t * H8, recv_x, myslot, K, H8, vl);
+  copy_row<TPT, NV>(x + (int64_t)t * H8, recv_x, myslot, K, H8, vl);
   if (vl < 64) write_meta(t, K, lane, myslot, w, recv_src, recv_w);
 }
 
@@ -801,20 +865,54 @@ __device__ __forceinline__ void quant_row_fp8(const u32x4* __restrict__ row,
 template <int NI>
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
-    const int32_t* __restrict__ off, const int32_t* __restrict__ recv_cnt,
     u32x4* __restrict__ recv_q, float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
-    float* __restrict__ recv_w, int N, int K, int E, int H, int64_t cap, int fill_blocks) {
+    float* __restrict__ recv_w, int N, int K, int H, int64_t cap, DispatchAux aux) {
   __shared__ int s_off[EP_MAX_EXPERTS + 1];
   __shared__ int s_cnt[EP_MAX_EXPERTS];
-  if ((int)blockIdx.x < fill_blocks) {
-    fill_padding<kThreads>(blockIdx.x, off, recv_cnt, E, cap, recv_src, recv_w, s_off, s_cnt);
+  const int nb = aux.blocks();
+  if ((int)blockIdx.x < nb) {
+    dispatch_aux<kThreads>(blockIdx.x, aux, s_off, s_cnt);
     return;
   }
-  const int t = uniform(((int)blockIdx.x - fill_blocks) * kWaves + (threadIdx.x >> 6));
+  const int t = uniform(((int)blockIdx.x - nb) * kWaves + (threadIdx.x >> 6));
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
   quant_row_fp8<NI>(x + (int64_t)t * (H >> 3), recv_q, recv_scales, myslot, K, H, lane);
+  write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+}
+
+// Pre-quantised rows (DeepEP's dispatch also takes x as a pair of e4m3 codes
+// and per-128-channel scales): one wavefront per token copies the H code
+// bytes (H/16 chunks, NV per lane) and the H/128 scales to each of the
+// token's slots, unchanged.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void dispatch_prequant_kernel(
+    const u32x4* __restrict__ xq, const float* __restrict__ xs, const float* __restrict__ w,
+    const int32_t* __restrict__ slot_of, u32x4* __restrict__ recv_q,
+    float* __restrict__ recv_scales, int32_t* __restrict__ recv_src, float* __restrict__ recv_w,
+    int N, int K, int H, int64_t cap, DispatchAux aux) {
+  __shared__ int s_off[EP_MAX_EXPERTS + 1];
+  __shared__ int s_cnt[EP_MAX_EXPERTS];
+  const int nb = aux.blocks();
+  if ((int)blockIdx.x < nb) {
+    dispatch_aux<kThreads>(blockIdx.x, aux, s_off, s_cnt);
+    return;
+  }
+  const int t = uniform(((int)blockIdx.x - nb) * kWaves + (threadIdx.x >> 6));
+  if (t >= N) return;
+  const int lane = threadIdx.x & 63;
+  const int myslot = load_slot(slot_of, t, K, lane, cap);
+  const int H16 = H >> 4, G = H >> 7;
+  copy_row<64, NV>(xq + (int64_t)t * H16, recv_q, myslot, K, H16, lane);
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    const float sv = xs[(int64_t)t * G + min(g, G - 1)];
+    for (int k = 0; k < K; k++) {
+      const int s = lane_value(myslot, k);
+      if (s >= 0 && g < G) recv_scales[(int64_t)s * G + g] = sv;
+    }
+  }
   write_meta(t, K, lane, myslot, w, recv_src, recv_w);
 }
 
@@ -831,9 +929,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
 constexpr int kLLThreads = 256;
 constexpr int kLLWaves = kLLThreads / 64;
 
-template <bool FP8, int NV>
+template <bool FP8, int NV, typename I>
 __global__ __launch_bounds__(kLLThreads) void ll_dispatch_kernel(
-    const int32_t* __restrict__ topk_idx, const u32x4* __restrict__ x,
+    const I* __restrict__ topk_idx, const u32x4* __restrict__ x,
     const float* __restrict__ w, int32_t* __restrict__ recv_count, int32_t* __restrict__ slot_of,
     int32_t* __restrict__ flags, u32x4* __restrict__ recv_x, float* __restrict__ recv_scales,
     int32_t* __restrict__ recv_src, float* __restrict__ recv_w, int K, int E, int R, int T,
@@ -900,7 +998,7 @@ __global__ __launch_bounds__(kLLThreads) void ll_dispatch_kernel(
     if constexpr (FP8)
       quant_row_fp8<NV>(x + (int64_t)t * (H >> 3), recv_x, recv_scales, myslot, K, H, lane);
     else
-      copy_row_bf16<64, NV>(x + (int64_t)t * (H >> 3), recv_x, myslot, K, H >> 3, lane);
+      copy_row<64, NV>(x + (int64_t)t * (H >> 3), recv_x, myslot, K, H >> 3, lane);
     write_meta(t, K, lane, myslot, w, recv_src, recv_w);
   }
 }
@@ -1097,6 +1195,8 @@ int validate_layout(const ep_problem_t* p) {
       R > EP_MAX_RANKS || R > E || A < 1)
     return EP_ERR_INVALID_ARG;
   if (E % R != 0 || N % R != 0) return EP_ERR_INVALID_ARG;
+  if (p->topk_idx_bytes != 0 && p->topk_idx_bytes != 4 && p->topk_idx_bytes != 8)
+    return EP_ERR_INVALID_ARG;
   if (bound_of(p) > INT32_MAX) return EP_ERR_INVALID_ARG;
   return EP_OK;
 }
@@ -1137,24 +1237,74 @@ Plan make_plan(const ep_problem_t* p) {
 }
 
 template <int NV>
-void launch_dispatch_bf16(dim3 grid, hipStream_t st, const ep_problem_t* p, const void* x,
-                          const float* w, const int32_t* slot_of, const int32_t* off,
-                          const int32_t* cnt, void* recv_x, int32_t* recv_src, float* recv_w,
-                          int64_t cap, int fill_blocks) {
+void launch_dispatch_bf16(int grid, hipStream_t st, const ep_problem_t* p,
+                          const ep_dispatch_args_t* a, const DispatchAux& aux) {
   constexpr int blk = EP_DISPATCH_TPT > kThreads ? EP_DISPATCH_TPT : kThreads;
   dispatch_bf16_kernel<EP_DISPATCH_TPT, NV, blk><<<grid, blk, 0, st>>>(
-      (const u32x4*)x, w, slot_of, off, cnt, (u32x4*)recv_x, recv_src, recv_w, p->num_tokens,
-      p->num_topk, p->num_experts, p->hidden / 8, cap, fill_blocks);
+      (const u32x4*)a->x, a->topk_weights, a->slot_of, (u32x4*)a->recv_x, a->recv_src_idx,
+      a->recv_topk_weights, p->num_tokens, p->num_topk, p->hidden / 8, a->recv_capacity, aux);
 }
 
 template <int NI>
-void launch_dispatch_fp8(dim3 grid, hipStream_t st, const ep_problem_t* p, const void* x,
-                         const float* w, const int32_t* slot_of, const int32_t* off,
-                         const int32_t* cnt, void* recv_x, float* recv_scales,
-                         int32_t* recv_src, float* recv_w, int64_t cap, int fill_blocks) {
+void launch_dispatch_fp8(int grid, hipStream_t st, const ep_problem_t* p,
+                         const ep_dispatch_args_t* a, const DispatchAux& aux) {
   dispatch_fp8_kernel<NI><<<grid, kThreads, 0, st>>>(
-      (const u32x4*)x, w, slot_of, off, cnt, (u32x4*)recv_x, recv_scales, recv_src, recv_w,
-      p->num_tokens, p->num_topk, p->num_experts, p->hidden, cap, fill_blocks);
+      (const u32x4*)a->x, a->topk_weights, a->slot_of, (u32x4*)a->recv_x, a->recv_scales,
+      a->recv_src_idx, a->recv_topk_weights, p->num_tokens, p->num_topk, p->hidden,
+      a->recv_capacity, aux);
+}
+
+template <int NV>
+void launch_dispatch_prequant(int grid, hipStream_t st, const ep_problem_t* p,
+                              const ep_dispatch_args_t* a, const DispatchAux& aux) {
+  dispatch_prequant_kernel<NV><<<grid, kThreads, 0, st>>>(
+      (const u32x4*)a->x, a->x_scales, a->topk_weights, a->slot_of, (u32x4*)a->recv_x,
+      a->recv_scales, a->recv_src_idx, a->recv_topk_weights, p->num_tokens, p->num_topk,
+      p->hidden, a->recv_capacity, aux);
+}
+
+// Layout launches for one index type.
+template <typename I>
+int run_layout(const ep_problem_t* p, const I* topk_idx, int32_t* num_tokens_per_rank,
+               int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+               int32_t* num_recv_per_expert, int32_t* expert_slot_offset, int32_t* slot_of,
+               void* workspace, hipStream_t st) {
+  int rc;
+  const int N = p->num_tokens;
+  const Plan pl = make_plan(p);
+  const int K = p->num_topk, E = p->num_experts, R = p->num_ranks;
+  const int T = N / R, L = E / R;
+  char* ws = (char*)workspace;
+  int32_t* err = (int32_t*)(ws + pl.o_err);
+  int32_t* blk_cnt = (int32_t*)(ws + pl.o_cnt);
+  int32_t* blk_rank = (int32_t*)(ws + pl.o_rank);
+  int32_t* blk_err = (int32_t*)(ws + pl.o_berr);
+  EP_LOG("layout N=%d K=%d E=%d R=%d A=%d idx=int%d: blocks=%d chunk=%d tokens", N, K, E, R,
+         p->expert_alignment, (int)(8 * sizeof(I)), pl.B, pl.C);
+  if (pl.B == 0) {
+    layout_empty_kernel<<<1, kThreads, 0, st>>>(err, num_tokens_per_rank, num_tokens_per_expert,
+                                                num_recv_per_expert, expert_slot_offset, E, R);
+    return check_launch("layout_empty");
+  }
+  if ((int64_t)N * K <= kFusedMaxPairs && N <= kFlagBytes && E <= kFusedMaxExperts &&
+      (int64_t)pl.C * K <= kAssignTile) {
+    const size_t mbytes = sizeof(unsigned long long) * (kFusedThreads / 64) * (size_t)E;
+    layout_fused_kernel<I><<<pl.B, kFusedThreads, mbytes, st>>>(
+        topk_idx, is_token_in_rank, err, num_tokens_per_rank, num_tokens_per_expert,
+        num_recv_per_expert, expert_slot_offset, slot_of, N, K, E, R, L, T, pl.CB, pl.C,
+        p->expert_alignment);
+    return check_launch("layout_fused");
+  }
+  layout_count_kernel<I><<<pl.B, kCountThreads, 0, st>>>(
+      topk_idx, is_token_in_rank, blk_cnt, blk_rank, blk_err, K, E, R, L, T, pl.CB, pl.C);
+  if ((rc = check_launch("layout_count")) != EP_OK) return rc;
+  size_t mask_bytes = sizeof(unsigned long long) * kAssignWaves * (size_t)E;
+  if (mask_bytes < 3 * sizeof(int) * kAssignThreads) mask_bytes = 3 * sizeof(int) * kAssignThreads;
+  layout_assign_kernel<I><<<pl.B, kAssignThreads, mask_bytes, st>>>(
+      topk_idx, blk_cnt, blk_rank, blk_err, err, num_tokens_per_rank, num_tokens_per_expert,
+      num_recv_per_expert, expert_slot_offset, slot_of, K, E, R, T, pl.CB, pl.C, pl.B,
+      p->expert_alignment);
+  return check_launch("layout_assign");
 }
 
 template <int Q, bool MULTI>
@@ -1194,13 +1344,18 @@ void launch_combine(int q, int N, hipStream_t st, const void* eo, const int32_t*
 }
 
 template <bool FP8, int NV>
-void launch_ll(int grid, size_t lds, hipStream_t st, const int32_t* idx, const void* x,
-               const float* w, int32_t* recv_count, int32_t* slot_of, int32_t* flags,
-               void* recv_x, float* recv_scales, int32_t* recv_src, float* recv_w, int K, int E,
-               int R, int T, int M, int H, int Q) {
-  ll_dispatch_kernel<FP8, NV><<<grid, kLLThreads, lds, st>>>(
-      idx, (const u32x4*)x, w, recv_count, slot_of, flags, (u32x4*)recv_x, recv_scales, recv_src,
-      recv_w, K, E, R, T, M, H, Q);
+void launch_ll(int grid, size_t lds, hipStream_t st, int idx_bytes, const void* idx,
+               const void* x, const float* w, int32_t* recv_count, int32_t* slot_of,
+               int32_t* flags, void* recv_x, float* recv_scales, int32_t* recv_src,
+               float* recv_w, int K, int E, int R, int T, int M, int H, int Q) {
+  if (idx_bytes == 8)
+    ll_dispatch_kernel<FP8, NV, int64_t><<<grid, kLLThreads, lds, st>>>(
+        (const int64_t*)idx, (const u32x4*)x, w, recv_count, slot_of, flags, (u32x4*)recv_x,
+        recv_scales, recv_src, recv_w, K, E, R, T, M, H, Q);
+  else
+    ll_dispatch_kernel<FP8, NV, int32_t><<<grid, kLLThreads, lds, st>>>(
+        (const int32_t*)idx, (const u32x4*)x, w, recv_count, slot_of, flags, (u32x4*)recv_x,
+        recv_scales, recv_src, recv_w, K, E, R, T, M, H, Q);
 }
 
 }  // namespace
@@ -1218,7 +1373,7 @@ int64_t ep_workspace_bytes(const ep_problem_t* p) {
   return make_plan(p).bytes;
 }
 
-int ep_get_layout(const ep_problem_t* p, const int32_t* topk_idx, int32_t* num_tokens_per_rank,
+int ep_get_layout(const ep_problem_t* p, const void* topk_idx, int32_t* num_tokens_per_rank,
                   int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
                   int32_t* num_recv_per_expert, int32_t* expert_slot_offset, int32_t* slot_of,
                   void* workspace, void* stream) {
@@ -1233,78 +1388,81 @@ int ep_get_layout(const ep_problem_t* p, const int32_t* topk_idx, int32_t* num_t
   rc = check_device();
   if (rc != EP_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  const Plan pl = make_plan(p);
-  const int K = p->num_topk, E = p->num_experts, R = p->num_ranks;
-  const int T = N / R, L = E / R;
-  char* ws = (char*)workspace;
-  int32_t* err = (int32_t*)(ws + pl.o_err);
-  int32_t* blk_cnt = (int32_t*)(ws + pl.o_cnt);
-  int32_t* blk_rank = (int32_t*)(ws + pl.o_rank);
-  int32_t* blk_err = (int32_t*)(ws + pl.o_berr);
-  EP_LOG("layout N=%d K=%d E=%d R=%d A=%d: blocks=%d chunk=%d tokens", N, K, E, R,
-         p->expert_alignment, pl.B, pl.C);
-  if (pl.B == 0) {
-    layout_empty_kernel<<<1, kThreads, 0, st>>>(err, num_tokens_per_rank, num_tokens_per_expert,
-                                                num_recv_per_expert, expert_slot_offset, E, R);
-    return check_launch("layout_empty");
-  }
-  if ((int64_t)N * K <= kFusedMaxPairs && N <= kFlagBytes && E <= kFusedMaxExperts &&
-      (int64_t)pl.C * K <= kAssignTile) {
-    const size_t mbytes = sizeof(unsigned long long) * (kFusedThreads / 64) * (size_t)E;
-    layout_fused_kernel<<<pl.B, kFusedThreads, mbytes, st>>>(
-        topk_idx, is_token_in_rank, err, num_tokens_per_rank, num_tokens_per_expert,
-        num_recv_per_expert, expert_slot_offset, slot_of, N, K, E, R, L, T, pl.CB, pl.C,
-        p->expert_alignment);
-    return check_launch("layout_fused");
-  }
-  layout_count_kernel<<<pl.B, kCountThreads, 0, st>>>(topk_idx, is_token_in_rank, blk_cnt, blk_rank,
-                                                 blk_err, K, E, R, L, T, pl.CB, pl.C);
-  if ((rc = check_launch("layout_count")) != EP_OK) return rc;
-  size_t mask_bytes = sizeof(unsigned long long) * kAssignWaves * (size_t)E;
-  if (mask_bytes < 3 * sizeof(int) * kAssignThreads) mask_bytes = 3 * sizeof(int) * kAssignThreads;
-  layout_assign_kernel<<<pl.B, kAssignThreads, mask_bytes, st>>>(
-      topk_idx, blk_cnt, blk_rank, blk_err, err, num_tokens_per_rank, num_tokens_per_expert,
-      num_recv_per_expert, expert_slot_offset, slot_of, K, E, R, T, pl.CB, pl.C, pl.B,
-      p->expert_alignment);
-  if ((rc = check_launch("layout_assign")) != EP_OK) return rc;
-  return EP_OK;
+  if (p->topk_idx_bytes == 8)
+    return run_layout(p, (const int64_t*)topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                      is_token_in_rank, num_recv_per_expert, expert_slot_offset, slot_of,
+                      workspace, st);
+  return run_layout(p, (const int32_t*)topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                    is_token_in_rank, num_recv_per_expert, expert_slot_offset, slot_of,
+                    workspace, st);
 }
 
-int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
-                const int32_t* slot_of, const int32_t* expert_slot_offset,
-                const int32_t* num_recv_per_expert, void* recv_x, float* recv_scales,
-                int32_t* recv_src_idx, float* recv_topk_weights, int64_t recv_capacity,
-                void* stream) {
+int ep_dispatch_ex(const ep_problem_t* p, const ep_dispatch_args_t* a, void* stream) {
   int rc = validate_payload(p);
   if (rc != EP_OK) return rc;
-  if (recv_capacity < bound_of(p)) return EP_ERR_CAPACITY;
-  const int N = p->num_tokens;
-  const bool meta = recv_src_idx || recv_topk_weights;
-  if (recv_topk_weights && N > 0 && !topk_weights) return EP_ERR_INVALID_ARG;
-  if (N > 0 && (!x || !slot_of || !recv_x)) return EP_ERR_INVALID_ARG;
-  if (p->use_fp8 && N > 0 && !recv_scales) return EP_ERR_INVALID_ARG;
-  if (meta && recv_capacity > 0 && (!expert_slot_offset || !num_recv_per_expert))
+  if (!a || (a->flags & ~(uint32_t)EP_DISPATCH_ZERO_PADDING) != 0) return EP_ERR_INVALID_ARG;
+  const int64_t cap = a->recv_capacity;
+  if (cap < bound_of(p)) return EP_ERR_CAPACITY;
+  const int N = p->num_tokens, E = p->num_experts, A = p->expert_alignment, H = p->hidden;
+  const bool meta = a->recv_src_idx || a->recv_topk_weights;
+  const bool prequant = a->x_scales != nullptr;
+  const bool zero = (a->flags & EP_DISPATCH_ZERO_PADDING) && A > 1;
+  const bool stats = a->cumulative_recv_stats != nullptr;
+  if (prequant && !p->use_fp8) return EP_ERR_INVALID_ARG;
+  if (a->recv_topk_weights && N > 0 && !a->topk_weights) return EP_ERR_INVALID_ARG;
+  if (N > 0 && (!a->x || !a->slot_of || !a->recv_x)) return EP_ERR_INVALID_ARG;
+  if (p->use_fp8 && N > 0 && !a->recv_scales) return EP_ERR_INVALID_ARG;
+  if ((meta || zero || stats) && (!a->expert_slot_offset || !a->num_recv_per_expert))
     return EP_ERR_INVALID_ARG;
+  if (zero && (!a->recv_x || (p->use_fp8 && !a->recv_scales))) return EP_ERR_INVALID_ARG;
   rc = check_device();
   if (rc != EP_OK) return rc;
   constexpr int dblk = EP_DISPATCH_TPT > kThreads ? EP_DISPATCH_TPT : kThreads;
   const int tok_per_block = p->use_fp8 ? kWaves : dblk / EP_DISPATCH_TPT;
-  const int tok_blocks = (N + tok_per_block - 1) / tok_per_block;
-  const int64_t fill_slots = (int64_t)(p->use_fp8 ? kThreads : dblk) * kFillPerThread;
-  const int64_t fill_blocks64 = meta ? (recv_capacity + fill_slots - 1) / fill_slots : 0;
-  if (fill_blocks64 + tok_blocks > INT32_MAX) return EP_ERR_INVALID_ARG;
-  const int grid = tok_blocks + (int)fill_blocks64;
+  const int blk = p->use_fp8 ? kThreads : dblk;
+  const int64_t tok_blocks = (N + tok_per_block - 1) / tok_per_block;
+  const int64_t fill_slots = (int64_t)blk * kFillPerThread;
+  const int64_t fill_blocks = meta ? (cap + fill_slots - 1) / fill_slots : 0;
+  const int64_t zero_waves = zero ? (int64_t)E * (A - 1) : 0;
+  const int64_t zero_blocks = (zero_waves + blk / 64 - 1) / (blk / 64);
+  const int64_t grid = tok_blocks + fill_blocks + zero_blocks + (stats ? 1 : 0);
+  if (grid > INT32_MAX) return EP_ERR_INVALID_ARG;
   if (grid == 0) return EP_OK;
+  DispatchAux aux{};
+  aux.off = a->expert_slot_offset;
+  aux.cnt = a->num_recv_per_expert;
+  aux.recv_src = a->recv_src_idx;
+  aux.recv_w = a->recv_topk_weights;
+  aux.recv_x = (u32x4*)a->recv_x;
+  aux.recv_scales = p->use_fp8 ? a->recv_scales : nullptr;
+  aux.stats = a->cumulative_recv_stats;
+  aux.cap = cap;
+  aux.E = E;
+  aux.A = A;
+  aux.row16 = p->use_fp8 ? H / 16 : H / 8;
+  aux.G = p->use_fp8 ? H / 128 : 0;
+  aux.fill_blocks = (int)fill_blocks;
+  aux.zero_blocks = (int)zero_blocks;
+  aux.stat_blocks = stats ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
-  const int H = p->hidden;
-  if (!p->use_fp8) {
+  EP_LOG("dispatch %s N=%d H=%d K=%d cap=%lld: token blocks=%lld fill=%lld zero=%lld stats=%d",
+         prequant ? "pre-quantised e4m3" : (p->use_fp8 ? "e4m3" : "bf16"), N, H, p->num_topk,
+         (long long)cap, (long long)tok_blocks, (long long)fill_blocks, (long long)zero_blocks,
+         (int)stats);
+  const int g = (int)grid;
+  if (prequant) {
+    const int q = (H / 16 + 63) / 64;
+#define EP_DQ(NV) launch_dispatch_prequant<NV>(g, st, p, a, aux)
+    if (q <= 1) EP_DQ(1);
+    else if (q <= 2) EP_DQ(2);
+    else if (q <= 4) EP_DQ(4);
+    else if (q <= 7) EP_DQ(7);
+    else if (q <= 8) EP_DQ(8);
+    else EP_DQ(16);
+#undef EP_DQ
+  } else if (!p->use_fp8) {
     const int q = (H / 8 + EP_DISPATCH_TPT - 1) / EP_DISPATCH_TPT;
-    EP_LOG("dispatch bf16 N=%d H=%d K=%d cap=%lld: token blocks=%d fill blocks=%lld nv=%d", N, H,
-           p->num_topk, (long long)recv_capacity, tok_blocks, (long long)fill_blocks64, q);
-#define EP_D16(NV)                                                                          \
-  launch_dispatch_bf16<NV>(grid, st, p, x, topk_weights, slot_of, expert_slot_offset,      \
-                           num_recv_per_expert, recv_x, recv_src_idx, recv_topk_weights,   \
-                           recv_capacity, (int)fill_blocks64)
+#define EP_D16(NV) launch_dispatch_bf16<NV>(g, st, p, a, aux)
     if (q <= 1) EP_D16(1);
     else if (q <= 2) EP_D16(2);
     else if (q <= 4) EP_D16(4);
@@ -1315,12 +1473,7 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
 #undef EP_D16
   } else {
     const int q = (H + 1023) / 1024;
-    EP_LOG("dispatch e4m3 N=%d H=%d K=%d cap=%lld: token blocks=%d fill blocks=%lld ni=%d", N, H,
-           p->num_topk, (long long)recv_capacity, tok_blocks, (long long)fill_blocks64, q);
-#define EP_D8(NI)                                                                           \
-  launch_dispatch_fp8<NI>(grid, st, p, x, topk_weights, slot_of, expert_slot_offset,       \
-                          num_recv_per_expert, recv_x, recv_scales, recv_src_idx,          \
-                          recv_topk_weights, recv_capacity, (int)fill_blocks64)
+#define EP_D8(NI) launch_dispatch_fp8<NI>(g, st, p, a, aux)
     if (q <= 1) EP_D8(1);
     else if (q <= 2) EP_D8(2);
     else if (q <= 4) EP_D8(4);
@@ -1329,6 +1482,25 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
 #undef EP_D8
   }
   return check_launch("dispatch");
+}
+
+int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
+                const int32_t* slot_of, const int32_t* expert_slot_offset,
+                const int32_t* num_recv_per_expert, void* recv_x, float* recv_scales,
+                int32_t* recv_src_idx, float* recv_topk_weights, int64_t recv_capacity,
+                void* stream) {
+  ep_dispatch_args_t a{};
+  a.x = x;
+  a.topk_weights = topk_weights;
+  a.slot_of = slot_of;
+  a.expert_slot_offset = expert_slot_offset;
+  a.num_recv_per_expert = num_recv_per_expert;
+  a.recv_x = recv_x;
+  a.recv_scales = recv_scales;
+  a.recv_src_idx = recv_src_idx;
+  a.recv_topk_weights = recv_topk_weights;
+  a.recv_capacity = recv_capacity;
+  return ep_dispatch_ex(p, &a, stream);
 }
 
 int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slot_of,
@@ -1357,7 +1529,7 @@ int64_t ep_ll_capacity(const ep_problem_t* p, int32_t max_tokens_per_rank) {
   return cap > INT32_MAX ? -1 : cap;
 }
 
-int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const int32_t* topk_idx,
+int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const void* topk_idx,
                    const void* x, const float* topk_weights, int32_t* recv_count,
                    int32_t* slot_of, int32_t* flags, void* recv_x, float* recv_scales,
                    int32_t* recv_src_idx, float* recv_topk_weights, void* stream) {
@@ -1385,8 +1557,9 @@ int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const int
   EP_LOG("ll dispatch N=%d H=%d K=%d E=%d R=%d M=%d fp8=%d: blocks=%d", N, H, K, E, R, M,
          p->use_fp8, grid);
 #define EP_LL(FP, NV)                                                                        \
-  launch_ll<FP, NV>(grid, lds, st, topk_idx, x, topk_weights, recv_count, slot_of, flags,   \
-                    recv_x, recv_scales, recv_src_idx, recv_topk_weights, K, E, R, T, M, H, Q)
+  launch_ll<FP, NV>(grid, lds, st, p->topk_idx_bytes, topk_idx, x, topk_weights, recv_count,  \
+                    slot_of, flags, recv_x, recv_scales, recv_src_idx, recv_topk_weights, K, E, \
+                    R, T, M, H, Q)
   if (!p->use_fp8) {
     const int q = (H / 8 + 63) / 64;
     if (q <= 1) EP_LL(false, 1);

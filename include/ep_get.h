@@ -81,6 +81,9 @@ enum {
  *                     multiple of A slots (DeepEP's expert_alignment)
  *   use_fp8           0: bf16 payload; 1: OCP E4M3FN payload with one fp32
  *                     scale per token and 128-channel group
+ *   topk_idx_bytes    width of topk_idx entries: 0 or 4 = int32, 8 = int64
+ *                     (DeepEP passes int64 indices); an int64 value outside
+ *                     the int32 range counts as an invalid expert id
  * Only the fields a call uses are checked (layout ignores hidden/use_fp8). */
 typedef struct ep_problem {
   int32_t num_tokens;
@@ -90,6 +93,7 @@ typedef struct ep_problem {
   int32_t num_ranks;
   int32_t expert_alignment;
   int32_t use_fp8;
+  int32_t topk_idx_bytes;
 } ep_problem_t;
 
 /* Receive capacity (slots) that always suffices without learning the counts:
@@ -106,7 +110,8 @@ int64_t ep_recv_capacity(const ep_problem_t* p);
 int64_t ep_workspace_bytes(const ep_problem_t* p);
 
 /* Routing layout (DeepEP book ch.1 sec. 1.4 names the first three outputs).
- *   topk_idx               [N][K] int32, global expert ids; -1 = no expert;
+ *   topk_idx               [N][K] int32 or int64 (topk_idx_bytes), global
+ *                          expert ids; -1 = no expert;
  *                          any other value outside [0, E) is skipped and sets
  *                          EP_LAYOUT_ERR_INDEX in the workspace error word
  *   num_tokens_per_rank    [R][R] int32 out: [s][r] = tokens of source s with
@@ -121,7 +126,7 @@ int64_t ep_workspace_bytes(const ep_problem_t* p);
  *   workspace              ep_workspace_bytes(p) bytes, 256-byte aligned
  * N == 0 is valid: offsets and counts come out zero.  Output pointers for
  * arrays of zero size may be NULL. */
-int ep_get_layout(const ep_problem_t* p, const int32_t* topk_idx,
+int ep_get_layout(const ep_problem_t* p, const void* topk_idx,
                   int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
                   uint8_t* is_token_in_rank, int32_t* num_recv_per_expert,
                   int32_t* expert_slot_offset, int32_t* slot_of, void* workspace,
@@ -153,6 +158,42 @@ int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
                 const int32_t* num_recv_per_expert, void* recv_x, float* recv_scales,
                 int32_t* recv_src_idx, float* recv_topk_weights, int64_t recv_capacity,
                 void* stream);
+
+/* Dispatch with the options of DeepEP's V2 dispatch (DeepEP book ch.1
+ * sec. 1.1: x may be a pair of FP8 data and scale factors; a running
+ * cumulative_local_expert_recv_stats tensor; do_zero_padding; a handle reused
+ * from an earlier call).  Every field not named below means what the
+ * argument of the same name of ep_dispatch means.
+ *   x_scales    NULL: x is bf16 and is quantised when use_fp8 (as ep_dispatch).
+ *               Otherwise x holds pre-quantised E4M3FN codes [N][H] and
+ *               x_scales their fp32 scales [N][H/128]; both are copied
+ *               unchanged to every slot of the token (requires use_fp8).
+ *   cumulative_recv_stats  [E] int64 or NULL: stats[e] += num_recv_per_expert[e]
+ *               once per call (in stream order; calls that overlap race).
+ *   flags       EP_DISPATCH_ZERO_PADDING: also set the padding rows of every
+ *               expert region, slots [off[e] + count[e], off[e+1]), to zero
+ *               bytes, and their scale rows to 0.0f when use_fp8.  Slots at or
+ *               beyond off[E] are left alone.
+ * A handle (slot_of, expert_slot_offset, num_recv_per_expert) from one
+ * ep_get_layout serves any number of dispatches of new token rows with the
+ * same routing; no call changes it. */
+#define EP_DISPATCH_ZERO_PADDING 1u
+typedef struct ep_dispatch_args {
+  const void* x;
+  const float* x_scales;
+  const float* topk_weights;
+  const int32_t* slot_of;
+  const int32_t* expert_slot_offset;
+  const int32_t* num_recv_per_expert;
+  void* recv_x;
+  float* recv_scales;
+  int32_t* recv_src_idx;
+  float* recv_topk_weights;
+  int64_t recv_capacity;
+  int64_t* cumulative_recv_stats;
+  uint32_t flags;
+} ep_dispatch_args_t;
+int ep_dispatch_ex(const ep_problem_t* p, const ep_dispatch_args_t* args, void* stream);
 
 /* Combine: y[t][c] = bf16( sum over k = 0..K-1 with slot_of[t][k] >= 0 of
  * topk_weights[t][k] * expert_out[slot_of[t][k]][c] ), accumulated in fp32 in
@@ -191,7 +232,7 @@ int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slo
  *               written (rows j >= recv_count of a sub-block keep old bytes)
  * Ignores expert_alignment. */
 int64_t ep_ll_capacity(const ep_problem_t* p, int32_t max_tokens_per_rank);
-int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const int32_t* topk_idx,
+int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const void* topk_idx,
                    const void* x, const float* topk_weights, int32_t* recv_count,
                    int32_t* slot_of, int32_t* flags, void* recv_x, float* recv_scales,
                    int32_t* recv_src_idx, float* recv_topk_weights, void* stream);

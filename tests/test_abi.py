@@ -133,3 +133,44 @@ def test_ll_capacity_and_validation():
     a = list(args)
     a[7] = None
     assert L.ep_ll_dispatch(ctypes.byref(p), 8, *a) == 1
+
+
+def test_index_width_validation():
+    for nb, ok in ((0, True), (4, True), (8, True), (2, False), (16, False)):
+        p = _p(topk_idx_bytes=nb)
+        assert (ep.lib().ep_recv_capacity(ctypes.byref(p)) >= 0) == ok
+
+
+def test_dispatch_ex_validation():
+    L = ep.lib()
+    fake = ctypes.c_void_p(256).value
+
+    def args(**kw):
+        a = ep.DispatchArgs()
+        for f in ("x", "topk_weights", "slot_of", "expert_slot_offset", "num_recv_per_expert",
+                  "recv_x", "recv_src_idx", "recv_topk_weights"):
+            setattr(a, f, fake)
+        a.recv_capacity = 10 ** 6
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    p = _p()
+    p8 = _p(use_fp8=True)
+    assert L.ep_dispatch_ex(ctypes.byref(p), None, None) == 1
+    # unknown flag bits
+    assert L.ep_dispatch_ex(ctypes.byref(p), ctypes.byref(args(flags=2)), None) == 1
+    # capacity below the bound
+    assert L.ep_dispatch_ex(ctypes.byref(p), ctypes.byref(args(recv_capacity=31)), None) == 2
+    # pre-quantised input needs use_fp8
+    assert L.ep_dispatch_ex(ctypes.byref(p), ctypes.byref(args(x_scales=fake)), None) == 1
+    # fp8 needs a scale buffer, also for zero padding
+    assert L.ep_dispatch_ex(ctypes.byref(p8), ctypes.byref(args(x_scales=fake)), None) == 1
+    # statistics and zero padding need the counts and offsets
+    assert L.ep_dispatch_ex(ctypes.byref(p), ctypes.byref(
+        args(recv_src_idx=None, recv_topk_weights=None, cumulative_recv_stats=fake,
+             num_recv_per_expert=None)), None) == 1
+    pa = _p(expert_alignment=4)
+    assert L.ep_dispatch_ex(ctypes.byref(pa), ctypes.byref(
+        args(recv_src_idx=None, recv_topk_weights=None, flags=1,
+             expert_slot_offset=None)), None) == 1
