@@ -199,6 +199,54 @@ def summarize(args):
     print(f"wrote profiles for {w.name}")
 
 
+def overlap_gemm(args, step, capture):
+    """Time K steps (one HIP graph) alone, K bf16 GEMMs alone (eager, on a
+    second stream) and both at once, each from one start event to the end of
+    both streams."""
+    import torch
+    m, k, n = (int(v) for v in args.overlap_gemm.lower().split("x"))
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    a = torch.randn((m, k), generator=gen).to(torch.bfloat16).cuda()
+    b = torch.randn((k, n), generator=gen).to(torch.bfloat16).cuda()
+    c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    reps = args.steps
+    g = capture(step, reps)
+    main_s = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def gemms():
+        with torch.cuda.stream(side):
+            for _ in range(reps):
+                torch.mm(a, b, out=c)
+
+    def timed(run_step, run_gemm):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        side.wait_event(e0)
+        if run_step:
+            g.replay()
+        if run_gemm:
+            gemms()
+        done = torch.cuda.Event()
+        done.record(side)
+        main_s.wait_event(done)
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    timed(True, True)   # warm both paths
+    step_ms = timed(True, False)
+    gemm_ms = timed(False, True)
+    both_ms = timed(True, True)
+    tflop = 2.0 * m * k * n / 1e12
+    return {"gemm": f"bf16 [{m},{k}]x[{k},{n}]", "cu_budget": args.cu_budget,
+            "step_ms": round(step_ms, 4), "gemm_ms": round(gemm_ms, 4),
+            "both_ms": round(both_ms, 4),
+            "gemm_tflops_alone": round(tflop / (gemm_ms * 1e-3), 1),
+            "overlap_saving": round(1.0 - both_ms / (step_ms + gemm_ms), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +260,12 @@ def main():
     ap.add_argument("--ll", type=int, default=0, metavar="M",
                     help="low-latency path: ep_ll_dispatch (routing + payload in one launch, "
                          "M rows per (expert, source) sub-block) + ep_combine")
+    ap.add_argument("--cu-budget", type=int, default=0, metavar="N",
+                    help="run dispatch and combine on at most N CUs (persistent grids, one "
+                         "workgroup per CU); 0 = whole GPU")
+    ap.add_argument("--overlap-gemm", default="", metavar="MxKxN",
+                    help="also time the K steps concurrently with K bf16 GEMMs "
+                         "[M,K]x[K,N] on a second stream (e.g. 8192x7168x4096)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying a HIP graph")
     ap.add_argument("--summarize", action="store_true",
@@ -268,10 +322,10 @@ def main():
         if args.ll:
             ep.ll_dispatch(x, idx, wts, w.E, w.R, args.ll, w.fp8, out=ll_out)
         else:
-            ep.dispatch(x, wts, lay, w.fp8, out=recv)
+            ep.dispatch(x, wts, lay, w.fp8, out=recv, cu_budget=args.cu_budget)
 
     def do_combine():
-        ep.combine(eo, lay, wts, out=y)
+        ep.combine(eo, lay, wts, out=y, cu_budget=args.cu_budget)
 
     def step():
         if not args.ll:
@@ -361,7 +415,9 @@ def main():
         dom_b, dom_ms = comb_b, com_ms
         dom_kernel = "combine"
     achieved = dom_b / (dom_ms * 1e-3) / 1e9
-    traffic = read_traffic(dom_kernel, w.name)
+    # the counters were taken on the ordinary grids, not on the CU-budget kernels
+    traffic = None if args.cu_budget else read_traffic(dom_kernel, w.name)
+    overlap = overlap_gemm(args, step, capture) if args.overlap_gemm else None
 
     result = {
         "metric": METRIC,
@@ -383,6 +439,7 @@ def main():
                    "num_ranks": w.R, "expert_alignment": 1 if args.ll else w.A,
                    "seed": args.seed, "path": (f"low-latency (M={args.ll})" if args.ll
                                                else "layout + dispatch + combine"),
+                   "cu_budget": args.cu_budget,
                    "parallelism": "1 GPU, virtual EP ranks"},
         "tokens_per_s": round(w.N / step_s, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -397,6 +454,8 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
     }
+    if overlap:
+        result["overlap"] = overlap
     if not args.no_ceiling:
         c = ceilings()
         result["ceiling"] = c

@@ -31,7 +31,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("num_topk", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("num_ranks", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
-                ("use_fp8", ctypes.c_int32), ("topk_idx_bytes", ctypes.c_int32)]
+                ("use_fp8", ctypes.c_int32), ("topk_idx_bytes", ctypes.c_int32),
+                ("cu_budget", ctypes.c_int32)]
 
 
 EP_DISPATCH_ZERO_PADDING = 1
@@ -107,10 +108,10 @@ def load(path):
 
 
 def problem(num_tokens, hidden, num_topk, num_experts, num_ranks, expert_alignment=1,
-            use_fp8=False, topk_idx_bytes=4):
+            use_fp8=False, topk_idx_bytes=4, cu_budget=0):
     return Problem(int(num_tokens), int(hidden), int(num_topk), int(num_experts),
                    int(num_ranks), int(expert_alignment), int(bool(use_fp8)),
-                   int(topk_idx_bytes))
+                   int(topk_idx_bytes), int(cu_budget))
 
 
 def _idx_bytes(topk_idx):
@@ -237,7 +238,7 @@ def alloc_recv(layout, hidden, use_fp8=False, device="cuda", capacity=None):
 
 
 def dispatch(x, topk_weights, layout, use_fp8=False, out=None, with_meta=True,
-             x_scales=None, zero_padding=False, cumulative_stats=None):
+             x_scales=None, zero_padding=False, cumulative_stats=None, cu_budget=0):
     """Scatter ``x`` [N, H] into expert-contiguous receive slots.
 
     Returns (recv_x, recv_scales, recv_src_idx, recv_topk_weights); recv_x is
@@ -247,6 +248,7 @@ def dispatch(x, topk_weights, layout, use_fp8=False, out=None, with_meta=True,
     With ``with_meta=False`` the per-slot source/weight tags are skipped;
     ``zero_padding`` zeroes the padding rows of every expert region;
     ``cumulative_stats`` ([E] int64) gets the per-expert receive counts added.
+    ``cu_budget`` > 0 keeps the kernel on at most that many CUs.
     """
     import torch
     N, H = x.shape
@@ -271,6 +273,7 @@ def dispatch(x, topk_weights, layout, use_fp8=False, out=None, with_meta=True,
         _need(rw, torch.float32, (cap,), "recv_topk_weights")
         _need(topk_weights, torch.float32, (layout.num_tokens, layout.num_topk), "topk_weights")
     p = layout.problem(H, use_fp8)
+    p.cu_budget = int(cu_budget)
     a = DispatchArgs()
     a.x = x.data_ptr()
     a.x_scales = None if x_scales is None else x_scales.data_ptr()
@@ -299,8 +302,9 @@ def dispatch(x, topk_weights, layout, use_fp8=False, out=None, with_meta=True,
     return recv_x, (scales if use_fp8 else None), src, rw
 
 
-def combine(expert_out, layout, topk_weights, out=None):
-    """Weighted top-k reduction of ``expert_out`` [cap, H] bf16 into token order."""
+def combine(expert_out, layout, topk_weights, out=None, cu_budget=0):
+    """Weighted top-k reduction of ``expert_out`` [cap, H] bf16 into token order;
+    ``cu_budget`` > 0 keeps the kernel on at most that many CUs."""
     import torch
     cap, H = expert_out.shape
     _need(expert_out, torch.bfloat16, (cap, H), "expert_out")
@@ -309,6 +313,7 @@ def combine(expert_out, layout, topk_weights, out=None):
         out = torch.empty((layout.num_tokens, H), dtype=torch.bfloat16, device=expert_out.device)
     _need(out, torch.bfloat16, (layout.num_tokens, H), "y")
     p = layout.problem(H)
+    p.cu_budget = int(cu_budget)
     rc = lib().ep_combine(ctypes.byref(p), _ptr(expert_out), _ptr(layout.slot_of),
                           _ptr(topk_weights), _ptr(out), cap, _stream())
     _check("ep_combine", rc)

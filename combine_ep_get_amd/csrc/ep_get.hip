@@ -607,20 +607,24 @@ __global__ __launch_bounds__(kThreads) void layout_empty_kernel(
 // off[E] belongs to the expert e with off[e] <= s < off[e+1] (binary search
 // over the offsets staged in LDS) and is padding iff s - off[e] >= count[e].
 template <int BLK>
-__device__ __forceinline__ void fill_padding(int fb, const int32_t* __restrict__ off,
-                                             const int32_t* __restrict__ recv_cnt, int E,
-                                             int64_t cap, int32_t* __restrict__ recv_src,
-                                             float* __restrict__ recv_w, int* s_off, int* s_cnt) {
-  const int tid = threadIdx.x;
-  for (int e = tid; e <= E; e += BLK) {
+__device__ __forceinline__ void stage_offsets(const int32_t* __restrict__ off,
+                                              const int32_t* __restrict__ recv_cnt, int E,
+                                              int* s_off, int* s_cnt) {
+  for (int e = threadIdx.x; e <= E; e += BLK) {
     s_off[e] = off[e];
     if (e < E) s_cnt[e] = recv_cnt[e];
   }
-  __syncthreads();
+}
+
+// Tag slots s0 + j*span + tid, j < kFillPerThread (offsets staged in LDS).
+__device__ __forceinline__ void tag_padding(int64_t s0, int span, int tid, int E, int64_t cap,
+                                            int32_t* __restrict__ recv_src,
+                                            float* __restrict__ recv_w, const int* s_off,
+                                            const int* s_cnt) {
   const int used = s_off[E];
 #pragma unroll
   for (int j = 0; j < kFillPerThread; j++) {
-    const int64_t s = (int64_t)fb * BLK * kFillPerThread + (int64_t)j * BLK + tid;
+    const int64_t s = s0 + (int64_t)j * span + tid;
     if (s >= cap) break;
     bool pad = true;
     if (s < used) {
@@ -636,6 +640,17 @@ __device__ __forceinline__ void fill_padding(int fb, const int32_t* __restrict__
       if (recv_w) recv_w[s] = 0.0f;
     }
   }
+}
+
+template <int BLK>
+__device__ __forceinline__ void fill_padding(int fb, const int32_t* __restrict__ off,
+                                             const int32_t* __restrict__ recv_cnt, int E,
+                                             int64_t cap, int32_t* __restrict__ recv_src,
+                                             float* __restrict__ recv_w, int* s_off, int* s_cnt) {
+  stage_offsets<BLK>(off, recv_cnt, E, s_off, s_cnt);
+  __syncthreads();
+  tag_padding((int64_t)fb * BLK * kFillPerThread, BLK, threadIdx.x, E, cap, recv_src, recv_w,
+              s_off, s_cnt);
 }
 
 // Work of a dispatch launch besides the token rows, done by the first blocks
@@ -662,10 +677,8 @@ struct DispatchAux {
 // (an expert region has fewer than A padding rows).  Consecutive waves take
 // consecutive rows of one expert, so blocks past an expert's padding exit
 // at once.
-template <int BLK>
-__device__ __forceinline__ void zero_padding_rows(int zb, const DispatchAux& a) {
+__device__ __forceinline__ void zero_padding_row(int64_t v, const DispatchAux& a) {
   const int lane = threadIdx.x & 63;
-  const int64_t v = (int64_t)zb * (BLK / 64) + (threadIdx.x >> 6);
   const int e = (int)(v / (a.A - 1)), j = (int)(v % (a.A - 1));
   if (e >= a.E) return;
   const int64_t row = (int64_t)a.off[e] + a.cnt[e] + j;
@@ -685,7 +698,7 @@ __device__ __forceinline__ void dispatch_aux(int b, const DispatchAux& a, int* s
   }
   b -= a.fill_blocks;
   if (b < a.zero_blocks) {
-    zero_padding_rows<BLK>(b, a);
+    zero_padding_row((int64_t)b * (BLK / 64) + (threadIdx.x >> 6), a);
     return;
   }
   for (int e = threadIdx.x; e < a.E; e += BLK) a.stats[e] += a.cnt[e];
@@ -882,6 +895,20 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
   write_meta(t, K, lane, myslot, w, recv_src, recv_w);
 }
 
+// The G scales of token t to each slot lanes 0..K-1 of `myslot` name.
+__device__ __forceinline__ void copy_scales(const float* __restrict__ xs, int t, int G,
+                                            float* __restrict__ recv_scales, int myslot, int K,
+                                            int lane) {
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    const float sv = xs[(int64_t)t * G + min(g, G - 1)];
+    for (int k = 0; k < K; k++) {
+      const int s = lane_value(myslot, k);
+      if (s >= 0 && g < G) recv_scales[(int64_t)s * G + g] = sv;
+    }
+  }
+}
+
 // Pre-quantised rows (DeepEP's dispatch also takes x as a pair of e4m3 codes
 // and per-128-channel scales): one wavefront per token copies the H code
 // bytes (H/16 chunks, NV per lane) and the H/128 scales to each of the
@@ -903,17 +930,70 @@ __global__ __launch_bounds__(kThreads) void dispatch_prequant_kernel(
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
-  const int H16 = H >> 4, G = H >> 7;
-  copy_row<64, NV>(xq + (int64_t)t * H16, recv_q, myslot, K, H16, lane);
-  for (int g0 = 0; g0 < G; g0 += 64) {
-    const int g = g0 + lane;
-    const float sv = xs[(int64_t)t * G + min(g, G - 1)];
-    for (int k = 0; k < K; k++) {
-      const int s = lane_value(myslot, k);
-      if (s >= 0 && g < G) recv_scales[(int64_t)s * G + g] = sv;
-    }
-  }
+  copy_row<64, NV>(xq + (int64_t)t * (H >> 4), recv_q, myslot, K, H >> 4, lane);
+  copy_scales(xs, t, H >> 7, recv_scales, myslot, K, lane);
   write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+}
+
+// ---------------------------------------------------------------- CU budget
+// DeepEP bounds the SMs its kernels occupy (num_sms) so that expert GEMMs can
+// run beside them.  Here the bound is a persistent grid of at most `budget`
+// workgroups of 1024 threads, each reserving all of a CU's LDS (160 KiB on
+// gfx950), so that no CU holds two of them, nor any other workgroup that uses
+// LDS (a GEMM's): the kernel occupies min(budget, work) CUs alone and leaves
+// the rest to other streams.  Its 16
+// wavefronts take work items i = blockIdx.x*16 + wave, stepping by
+// gridDim.x*16; an item is one token row (dispatch), one token's 64-chunk
+// column group (combine), or one piece of the auxiliary work: tags for 512
+// slots, one candidate padding row, or the statistics.  Every item runs the
+// same wavefront code as the ordinary grids, so results are identical.
+constexpr int kPersistThreads = 1024;
+constexpr int kPersistWaves = kPersistThreads / 64;
+constexpr int kCombinePersistNV = 2;  // 16-byte chunks per lane per combine item
+
+template <int MODE, int NV>  // MODE 0: bf16 copy, 1: fused e4m3, 2: pre-quantised e4m3
+__global__ __launch_bounds__(kPersistThreads) void dispatch_persist_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ xs, const float* __restrict__ w,
+    const int32_t* __restrict__ slot_of, u32x4* __restrict__ recv_x,
+    float* __restrict__ recv_scales, int32_t* __restrict__ recv_src, float* __restrict__ recv_w,
+    int N, int K, int H, int64_t cap, DispatchAux aux, int64_t fill_items, int64_t zero_items) {
+  extern __shared__ int lds[];  // [E+1] offsets, [E] counts; the rest only reserves the CU
+  int* s_off = lds;
+  int* s_cnt = lds + aux.E + 1;
+  if (fill_items > 0) stage_offsets<kPersistThreads>(aux.off, aux.cnt, aux.E, s_off, s_cnt);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t stat_items = aux.stats ? 1 : 0;
+  const int64_t n_items = fill_items + zero_items + stat_items + N;
+  for (int64_t i = (int64_t)blockIdx.x * kPersistWaves + (threadIdx.x >> 6); i < n_items;
+       i += (int64_t)gridDim.x * kPersistWaves) {
+    int64_t r = i;
+    if (r < fill_items) {
+      tag_padding(r * 64 * kFillPerThread, 64, lane, aux.E, cap, recv_src, recv_w, s_off, s_cnt);
+      continue;
+    }
+    r -= fill_items;
+    if (r < zero_items) {
+      zero_padding_row(r, aux);
+      continue;
+    }
+    r -= zero_items;
+    if (r < stat_items) {
+      for (int e = lane; e < aux.E; e += 64) aux.stats[e] += aux.cnt[e];
+      continue;
+    }
+    const int t = uniform((int)(r - stat_items));
+    const int myslot = load_slot(slot_of, t, K, lane, cap);
+    if constexpr (MODE == 0) {
+      copy_row<64, NV>(x + (int64_t)t * (H >> 3), recv_x, myslot, K, H >> 3, lane);
+    } else if constexpr (MODE == 1) {
+      quant_row_fp8<NV>(x + (int64_t)t * (H >> 3), recv_x, recv_scales, myslot, K, H, lane);
+    } else {
+      copy_row<64, NV>(x + (int64_t)t * (H >> 4), recv_x, myslot, K, H >> 4, lane);
+      copy_scales(xs, t, H >> 7, recv_scales, myslot, K, lane);
+    }
+    write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+  }
 }
 
 // ---------------------------------------------------------------- low latency
@@ -1142,6 +1222,39 @@ __global__ __launch_bounds__(BLK) void combine_kernel(
   }
 }
 
+// Combine under a CU budget (see dispatch_persist_kernel): an item is one
+// token's group of 64*NV 16-byte chunks (NV per lane); K rows of it are
+// gathered and reduced in ascending k exactly as in combine_kernel.
+template <int NV>
+__global__ __launch_bounds__(kPersistThreads) void combine_persist_kernel(
+    const u32x4* __restrict__ eo, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ w, u32x4* __restrict__ y, int N, int K, int H8, int64_t cap) {
+  extern __shared__ int lds[];  // only reserves the CU
+  if (N < 0) lds[threadIdx.x] = 0;
+  const int lane = threadIdx.x & 63;
+  const int Q = (H8 + 64 * NV - 1) / (64 * NV);
+  const int64_t n_items = (int64_t)N * Q;
+  for (int64_t i = (int64_t)blockIdx.x * kPersistWaves + (threadIdx.x >> 6); i < n_items;
+       i += (int64_t)gridDim.x * kPersistWaves) {
+    const int t = uniform((int)(i / Q)), base = uniform((int)(i % Q)) * 64 * NV;
+    const int myslot = load_slot(slot_of, t, K, lane, cap);
+    const float myw = (lane < K) ? w[(int64_t)t * K + lane] : 0.0f;
+    float acc[NV][8];
+#pragma unroll
+    for (int i2 = 0; i2 < NV; i2++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) acc[i2][j] = 0.0f;
+    for (int kg = 0; kg < K; kg += 8) {
+      u32x4 v[8][NV];
+      const int slot_g = __shfl_down(myslot, kg);
+      const float w_g = __shfl_down(myw, kg);
+      combine_load8<64, NV>(v, eo, slot_g, K - kg, base, lane, H8);
+      combine_accum8<NV>(acc, v, slot_g, w_g, K - kg);
+    }
+    combine_store<64, NV>(acc, y + (int64_t)t * H8, base, lane, H8);
+  }
+}
+
 // ---------------------------------------------------------------- host side
 bool log_on() {
   static int v = -1;
@@ -1174,6 +1287,22 @@ int check_device() {
   return c == 1 ? EP_OK : EP_ERR_UNSUPPORTED;
 }
 
+// LDS a persistent workgroup reserves: the whole per-workgroup maximum of
+// the current device (cached per device; 0 if it cannot be read).
+size_t persist_lds() {
+  static std::atomic<long long> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  long long v = (dev >= 0 && dev < 64) ? cache[dev].load() : 0;
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    v = (long long)prop.sharedMemPerBlock;
+    if (dev >= 0 && dev < 64) cache[dev].store(v);
+  }
+  return (size_t)v;
+}
+
 int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -1197,6 +1326,7 @@ int validate_layout(const ep_problem_t* p) {
   if (E % R != 0 || N % R != 0) return EP_ERR_INVALID_ARG;
   if (p->topk_idx_bytes != 0 && p->topk_idx_bytes != 4 && p->topk_idx_bytes != 8)
     return EP_ERR_INVALID_ARG;
+  if (p->cu_budget < 0) return EP_ERR_INVALID_ARG;
   if (bound_of(p) > INT32_MAX) return EP_ERR_INVALID_ARG;
   return EP_OK;
 }
@@ -1261,6 +1391,16 @@ void launch_dispatch_prequant(int grid, hipStream_t st, const ep_problem_t* p,
       (const u32x4*)a->x, a->x_scales, a->topk_weights, a->slot_of, (u32x4*)a->recv_x,
       a->recv_scales, a->recv_src_idx, a->recv_topk_weights, p->num_tokens, p->num_topk,
       p->hidden, a->recv_capacity, aux);
+}
+
+template <int MODE, int NV>
+void launch_dispatch_persist(int grid, hipStream_t st, const ep_problem_t* p,
+                             const ep_dispatch_args_t* a, const DispatchAux& aux,
+                             int64_t fill_items, int64_t zero_items) {
+  dispatch_persist_kernel<MODE, NV><<<grid, kPersistThreads, persist_lds(), st>>>(
+      (const u32x4*)a->x, a->x_scales, a->topk_weights, a->slot_of, (u32x4*)a->recv_x,
+      a->recv_scales, a->recv_src_idx, a->recv_topk_weights, p->num_tokens, p->num_topk,
+      p->hidden, a->recv_capacity, aux, fill_items, zero_items);
 }
 
 // Layout launches for one index type.
@@ -1445,6 +1585,45 @@ int ep_dispatch_ex(const ep_problem_t* p, const ep_dispatch_args_t* a, void* str
   aux.zero_blocks = (int)zero_blocks;
   aux.stat_blocks = stats ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
+  if (p->cu_budget > 0) {
+    // persistent grid: one 1024-thread workgroup per CU, wavefront work items
+    const int64_t fill_items = meta ? (cap + 64 * kFillPerThread - 1) / (64 * kFillPerThread) : 0;
+    const int64_t items = N + fill_items + zero_waves + (stats ? 1 : 0);
+    const int64_t want = (items + kPersistWaves - 1) / kPersistWaves;
+    const int pg = (int)(want < p->cu_budget ? want : p->cu_budget);
+    if (pg == 0) return EP_OK;
+    const size_t lds = persist_lds();
+    EP_LOG("dispatch (CU budget %d) N=%d H=%d K=%d cap=%lld: workgroups=%d items=%lld lds=%zu",
+           p->cu_budget, N, H, p->num_topk, (long long)cap, pg, (long long)items, lds);
+    if (lds < 4 * (2 * (size_t)EP_MAX_EXPERTS + 1)) return EP_ERR_HIP;
+    const int mode = prequant ? 2 : (p->use_fp8 ? 1 : 0);
+    const int q = mode == 0 ? (H / 8 + 63) / 64 : (mode == 2 ? (H / 16 + 63) / 64 : (H + 1023) / 1024);
+#define EP_DP(M, NV) launch_dispatch_persist<M, NV>(pg, st, p, a, aux, fill_items, zero_waves)
+    if (mode == 0) {
+      if (q <= 1) EP_DP(0, 1);
+      else if (q <= 2) EP_DP(0, 2);
+      else if (q <= 4) EP_DP(0, 4);
+      else if (q <= 7) EP_DP(0, 7);
+      else if (q <= 8) EP_DP(0, 8);
+      else if (q <= 14) EP_DP(0, 14);
+      else EP_DP(0, 16);
+    } else if (mode == 1) {
+      if (q <= 1) EP_DP(1, 1);
+      else if (q <= 2) EP_DP(1, 2);
+      else if (q <= 4) EP_DP(1, 4);
+      else if (q <= 7) EP_DP(1, 7);
+      else EP_DP(1, 8);
+    } else {
+      if (q <= 1) EP_DP(2, 1);
+      else if (q <= 2) EP_DP(2, 2);
+      else if (q <= 4) EP_DP(2, 4);
+      else if (q <= 7) EP_DP(2, 7);
+      else if (q <= 8) EP_DP(2, 8);
+      else EP_DP(2, 16);
+    }
+#undef EP_DP
+    return check_launch("dispatch_persist");
+  }
   EP_LOG("dispatch %s N=%d H=%d K=%d cap=%lld: token blocks=%lld fill=%lld zero=%lld stats=%d",
          prequant ? "pre-quantised e4m3" : (p->use_fp8 ? "e4m3" : "bf16"), N, H, p->num_topk,
          (long long)cap, (long long)tok_blocks, (long long)fill_blocks, (long long)zero_blocks,
@@ -1517,6 +1696,20 @@ int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slo
   hipStream_t st = (hipStream_t)stream;
   const int H8 = p->hidden / 8;
   const int q = (H8 + 63) / 64;  // wavefronts for one chunk per thread
+  if (p->cu_budget > 0) {
+    constexpr int nv = kCombinePersistNV;
+    const int64_t items = (int64_t)N * ((H8 + 64 * nv - 1) / (64 * nv));
+    const int64_t want = (items + kPersistWaves - 1) / kPersistWaves;
+    const int pg = (int)(want < p->cu_budget ? want : p->cu_budget);
+    const size_t lds = persist_lds();
+    EP_LOG("combine (CU budget %d) N=%d H=%d K=%d: workgroups=%d lds=%zu", p->cu_budget, N,
+           p->hidden, p->num_topk, pg, lds);
+    if (lds < 4 * (2 * (size_t)EP_MAX_EXPERTS + 1)) return EP_ERR_HIP;
+    combine_persist_kernel<nv><<<pg, kPersistThreads, lds, st>>>(
+        (const u32x4*)expert_out, slot_of, topk_weights, (u32x4*)y, N, p->num_topk, H8,
+        recv_capacity);
+    return check_launch("combine_persist");
+  }
   EP_LOG("combine N=%d H=%d K=%d cap=%lld: waves per token=%d%s", N, p->hidden, p->num_topk,
          (long long)recv_capacity, q > 16 ? 16 : (q == 3 ? 4 : q), q > 16 ? " (multi-pass)" : "");
   launch_combine(q, N, st, expert_out, slot_of, topk_weights, y, p->num_topk, H8, recv_capacity);

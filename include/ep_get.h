@@ -84,6 +84,14 @@ enum {
  *   topk_idx_bytes    width of topk_idx entries: 0 or 4 = int32, 8 = int64
  *                     (DeepEP passes int64 indices); an int64 value outside
  *                     the int32 range counts as an invalid expert id
+ *   cu_budget         0: dispatch and combine use the whole GPU.  n > 0: they
+ *                     run as persistent grids of at most n workgroups, one
+ *                     per CU (each reserves over half of a CU's LDS), so they
+ *                     occupy at most n CUs and leave the rest to concurrent
+ *                     work -- the role of DeepEP's num_sms (hotdry analysis,
+ *                     "two kernel families": a fixed SM share for
+ *                     communication).  Results are identical for every n.
+ *                     Layout and low-latency dispatch ignore it.
  * Only the fields a call uses are checked (layout ignores hidden/use_fp8). */
 typedef struct ep_problem {
   int32_t num_tokens;
@@ -94,6 +102,7 @@ typedef struct ep_problem {
   int32_t expert_alignment;
   int32_t use_fp8;
   int32_t topk_idx_bytes;
+  int32_t cu_budget;
 } ep_problem_t;
 
 /* Receive capacity (slots) that always suffices without learning the counts:

@@ -174,3 +174,12 @@ def test_dispatch_ex_validation():
     assert L.ep_dispatch_ex(ctypes.byref(pa), ctypes.byref(
         args(recv_src_idx=None, recv_topk_weights=None, flags=1,
              expert_slot_offset=None)), None) == 1
+
+
+def test_cu_budget_validation():
+    L = ep.lib()
+    p = _p(cu_budget=-1)
+    assert ep.lib().ep_recv_capacity(ctypes.byref(p)) == -1
+    assert L.ep_combine(ctypes.byref(p), None, None, None, None, 0, None) == 1
+    p = _p(cu_budget=4)
+    assert ep.lib().ep_recv_capacity(ctypes.byref(p)) == 32

@@ -1,0 +1,79 @@
+"""GPU parity of the CU-budget launches (ep_problem_t.cu_budget > 0: persistent
+grids, one workgroup per CU).  Every budget must give the bytes of the
+ordinary launch, which the main parity tests hold to the oracle; the small
+case is also compared with the oracle directly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_get_amd as ep
+import oracle
+from combine_ep_get_amd import workloads as wl
+
+from .gpu_util import check_combine, dev_bf16, host_u16, say
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = wl.custom(N=60, H=384, E=12, K=3, R=3, A=16, name="ragged")
+
+
+def _run(w, inp, mode, budget, lay, eo):
+    """dispatch (with tags, zero padding, statistics) + combine at one budget."""
+    fp8 = mode != "bf16"
+    wts = torch.from_numpy(inp["topk_weights"]).cuda()
+    out = ep.alloc_recv(lay, w.H, fp8)
+    out[0].view(torch.uint8).fill_(0x3C)
+    if fp8:
+        out[1].fill_(7.0)
+    out[2].fill_(-9)
+    out[3].fill_(9.0)
+    stats = torch.full((w.E,), 11, dtype=torch.int64, device="cuda")
+    kw = dict(out=out, zero_padding=True, cumulative_stats=stats, cu_budget=budget)
+    if mode == "prequant":
+        codes, scales = oracle.quantize_rows(inp["x"])
+        xq = torch.from_numpy(codes).cuda().view(torch.float8_e4m3fn)
+        ep.dispatch(xq, wts, lay, True, x_scales=torch.from_numpy(scales).cuda(), **kw)
+    else:
+        ep.dispatch(dev_bf16(inp["x"]), wts, lay, fp8, **kw)
+    y = ep.combine(eo, lay, wts, cu_budget=budget)
+    torch.cuda.synchronize()
+    res = [out[0].view(torch.uint8).cpu(), out[2].cpu(), out[3].cpu(), stats.cpu(),
+           y.view(torch.int16).cpu()]
+    if fp8:
+        res.append(out[1].cpu())
+    return res
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp8", "prequant"])
+@pytest.mark.parametrize("cid", [0, 3])
+def test_budget_matches_ordinary_launch(cid, mode):
+    w = RAGGED if cid == 0 else wl.CONFIGS[cid]
+    inp = wl.make_inputs(w, 0)
+    say(f"CU budget parity {w.desc} mode={mode}")
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    lay = ep.get_layout(idx, w.E, w.R, w.A)
+    eo_bits = wl.make_expert_out(w, lay.capacity, 0)
+    eo = dev_bf16(eo_bits)
+    ref = _run(w, inp, mode, 0, lay, eo)
+    budgets = [1, 3, 256] if cid == 0 else [5, 64, 255, 4096]
+    for b in budgets:
+        got = _run(w, inp, mode, b, lay, eo)
+        for i, (a, c) in enumerate(zip(ref, got)):
+            assert torch.equal(a, c), f"budget {b}: output {i} differs from the ordinary launch"
+        say(f"  budget {b}: identical")
+    if cid == 0:
+        # the ordinary launch itself against the oracle
+        r = oracle.layout(inp["topk_idx"], w.E, w.R, w.A)
+        ref_y, ref_acc = oracle.combine(eo_bits, r["slot_of"], inp["topk_weights"])
+        assert check_combine(ref[4].numpy().view(np.uint16), ref_y, ref_acc) == 0
+        want = np.full(w.E, 11, np.int64)
+        oracle.accumulate_stats(r["num_recv_per_expert"], want)
+        np.testing.assert_array_equal(ref[3].numpy(), want)
+        src, _ = oracle.recv_meta(r["slot_of"], inp["topk_weights"], lay.capacity)
+        np.testing.assert_array_equal(ref[1].numpy(), src)
+        if mode == "bf16":
+            rx = oracle.dispatch_bf16(inp["x"], r["slot_of"], lay.capacity, fill=0x3C3C)
+            oracle.zero_padding(rx, None, r["expert_slot_offset"], r["num_recv_per_expert"])
+            np.testing.assert_array_equal(ref[0].numpy().view(np.uint16), rx)
+
