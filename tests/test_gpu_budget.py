@@ -77,3 +77,28 @@ def test_budget_matches_ordinary_launch(cid, mode):
             oracle.zero_padding(rx, None, r["expert_slot_offset"], r["num_recv_per_expert"])
             np.testing.assert_array_equal(ref[0].numpy().view(np.uint16), rx)
 
+
+
+EDGE = [(wl.custom(N=48, H=136, E=16, K=12, R=4, A=3, name="k12_h136"), "bf16"),
+        (wl.custom(N=32, H=16392, E=8, K=2, R=2, A=1, name="h16392"), "bf16"),
+        (wl.custom(N=64, H=16384, E=8, K=3, R=4, A=4, name="fp8_h16384"), "fp8"),
+        (wl.custom(N=256, H=256, E=1024, K=32, R=256, A=2, name="e1024_k32"), "bf16"),
+        (wl.custom(N=40, H=1152, E=10, K=5, R=5, A=7, name="prequant_ragged"), "prequant")]
+
+
+@pytest.mark.parametrize("w,mode", EDGE, ids=[e[0].name for e in EDGE])
+def test_budget_edge_shapes(w, mode):
+    inp = wl.make_inputs(w, 1)
+    say(f"CU budget edge {w.desc} mode={mode}")
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    lay = ep.get_layout(idx, w.E, w.R, w.A)
+    eo_bits = wl.make_expert_out(w, lay.capacity, 1)
+    eo = dev_bf16(eo_bits)
+    ref = _run(w, inp, mode, 0, lay, eo)
+    for b in (1, 2, 37):
+        got = _run(w, inp, mode, b, lay, eo)
+        for i, (a, c) in enumerate(zip(ref, got)):
+            assert torch.equal(a, c), f"budget {b}: output {i} differs from the ordinary launch"
+    r = oracle.layout(inp["topk_idx"], w.E, w.R, w.A)
+    ref_y, ref_acc = oracle.combine(eo_bits, r["slot_of"], inp["topk_weights"])
+    assert check_combine(ref[4].numpy().view(np.uint16), ref_y, ref_acc) == 0
