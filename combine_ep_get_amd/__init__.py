@@ -10,6 +10,11 @@ raises -- there is no fallback of any kind.
     recv_x, recv_scales, recv_src_idx, recv_w = dispatch(x, topk_weights, lay, use_fp8)
     y = combine(expert_out, lay, topk_weights)
 
+Options (same kernels): ``topk_idx`` int32 or int64; ``dispatch(...,
+x_scales=sf)`` for pre-quantised e4m3 input, ``zero_padding=True``,
+``cumulative_stats=t``; ``cu_budget=n`` on dispatch and combine;
+``ll_dispatch`` for decode batches (routing and payload in one launch).
+
 The names follow DeepEP's (DeepEP book ch.1 "positioning and version
 boundaries", sec. 1.1 and 1.4): num_tokens_per_rank, num_tokens_per_expert,
 is_token_in_rank, expert_alignment, num_experts.

@@ -13,6 +13,13 @@
 //              practice (nlpx) sec. 4.1 for the per-block scale.
 //   combine  : fp32 weighted gather-reduce of the K expert rows, bf16 store.
 //              Lesson 14, sec. 3 (top-k weighted sum) and practice task.
+//   low-latency dispatch : routing and payload in one launch over fixed
+//              (expert, source) sub-blocks (lesson 14 sec. 3; hotdry analysis,
+//              "two kernel families").
+//   options  : int64 routing indices, pre-quantised e4m3 input, zeroed
+//              padding rows, running per-expert counts (DeepEP book ch.1
+//              sec. 1.1), and a CU budget that keeps dispatch and combine on
+//              a fixed number of CUs (hotdry analysis, "two kernel families").
 //
 // Nothing here is a contraction, so there is no MFMA: every kernel is bound by
 // HBM bandwidth (dispatch, combine) or by latency (layout).  Design points:
