@@ -49,7 +49,13 @@ def algorithmic_bytes(w):
 
 
 def source_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    """sha256 of the kernel source with comments and blank space removed, so
+    that edits to comments alone do not mark the counter summaries stale."""
+    src = open(KERNEL_SRC).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()
 
 
 def read_traffic(kernel, workload):
@@ -143,7 +149,7 @@ def summarize(args):
     lines = [f"# rocprofv3 kernel statistics: {w.desc}",
              f"# command: cd /tmp && rocprofv3 --kernel-trace --stats -T -f csv -d <out> -o run -- "
              f"{cmd_base} --steps 20 --warmup 5 --cpu-seconds 0 --no-ceiling",
-             f"# kernel source sha256: {source_sha()}",
+             f"# kernel source sha256 (comments and blank space stripped): {source_sha()}",
              f"{'kernel':28s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
     for r in stats:
         lines.append(f"{r['Name'][:28]:28s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
@@ -181,6 +187,7 @@ def summarize(args):
                f"#           cd /tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv -d <out> -o run -- "
                f"{cmd_base} --steps 3 --warmup 1 --cpu-seconds 0",
                "# scale: counter KiB of the 1 GiB copy kernel in the same run -> bytes",
+               "# source_sha256: ep_get.hip with comments and blank space stripped",
                f"kernel: {kname}",
                f"workload: {w.name}",
                f"source_sha256: {source_sha()}",
