@@ -1696,7 +1696,8 @@ int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slo
   const int N = p->num_tokens;
   if (recv_capacity < 0) return EP_ERR_INVALID_ARG;
   if (N == 0) return EP_OK;
-  if (!slot_of || !topk_weights || !y || (recv_capacity > 0 && !expert_out))
+  // the loads are branch-free: a pair without a slot reads row 0, which must exist
+  if (recv_capacity < 1 || !slot_of || !topk_weights || !y || !expert_out)
     return EP_ERR_INVALID_ARG;
   rc = check_device();
   if (rc != EP_OK) return rc;

@@ -208,7 +208,8 @@ int ep_dispatch_ex(const ep_problem_t* p, const ep_dispatch_args_t* args, void* 
  * topk_weights[t][k] * expert_out[slot_of[t][k]][c] ), accumulated in fp32 in
  * ascending k, each product and sum rounded separately, stored with
  * round-to-nearest-even (lesson 14's combine step, DeepEP walkthrough 2.1).
- *   expert_out     [recv_capacity][H] bf16
+ *   expert_out     [recv_capacity][H] bf16; recv_capacity >= 1 when N > 0
+ *                  (else EP_ERR_INVALID_ARG)
  *   slot_of        [N][K] int32 from ep_get_layout (entries outside
  *                  [0, recv_capacity) are treated as "no expert")
  *   topk_weights   [N][K] fp32

@@ -104,6 +104,8 @@ def test_payload_rejects_bad_descriptors():
     assert L.ep_dispatch(ctypes.byref(p), None, fake, fake, fake, fake, fake, None, fake, fake,
                          10 ** 6, None) == 1
     assert L.ep_combine(ctypes.byref(p), fake, None, fake, fake, 10 ** 6, None) == 1
+    # tokens but a zero-row expert_out: rejected (pairs without a slot read row 0)
+    assert L.ep_combine(ctypes.byref(p), fake, fake, fake, fake, 0, None) == 1
     # fp8 needs a scale buffer
     p8 = _p(use_fp8=True)
     assert L.ep_dispatch(ctypes.byref(p8), fake, fake, fake, fake, fake, fake, None, fake, fake,
