@@ -689,7 +689,7 @@ __device__ __forceinline__ void zero_padding_row(int64_t v, const DispatchAux& a
   const int e = (int)(v / (a.A - 1)), j = (int)(v % (a.A - 1));
   if (e >= a.E) return;
   const int64_t row = (int64_t)a.off[e] + a.cnt[e] + j;
-  if (row >= a.off[e + 1] || row >= a.cap) return;
+  if (row < 0 || row >= a.off[e + 1] || row >= a.cap) return;  // [0, cap) even for foreign offsets
   const u32x4 z = {0u, 0u, 0u, 0u};
   u32x4* dst = a.recv_x + row * a.row16;
   for (int c = lane; c < a.row16; c += 64) st16(dst + c, z);
