@@ -91,8 +91,16 @@ def cpu_baseline(w, inp, eo_bits, budget_s):
         t_total += time.perf_counter() - t0
         reps += 1
     step_s = t_total / reps
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round((disp_b + comb_b) / step_s / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"{reps} full steps (layout+dispatch+combine) of the {w.name} batch, "
                       f"{w.N} tokens, single thread, {step_s * 1e3:.1f} ms/step",
             "tokens_per_s": round(w.N / step_s, 1)}
@@ -273,6 +281,9 @@ def main():
     ap.add_argument("--overlap-gemm", default="", metavar="MxKxN",
                     help="also time the K steps concurrently with K bf16 GEMMs "
                          "[M,K]x[K,N] on a second stream (e.g. 8192x7168x4096)")
+    ap.add_argument("--cold-steps", type=int, default=50, metavar="C",
+                    help="also time C single steps, each after an untimed 1 GiB write that "
+                         "evicts L2 and the Infinity Cache (0 skips)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying a HIP graph")
     ap.add_argument("--summarize", action="store_true",
@@ -406,6 +417,30 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    # Cold-cache steps: one step at a time, each after an untimed 1 GiB write
+    # (more than the 256 MB Infinity Cache plus the L2s), timed by events on
+    # the launch stream; median and spread over the steps.
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold_steps)]
+        for i, (a, b) in enumerate(evs):
+            flush.fill_(i & 0xFF)
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        del flush
+        disp_b0, comb_b0 = algorithmic_bytes(w)
+        cold = {"median_us": round(float(np.median(us)), 2),
+                "p10_us": round(float(np.percentile(us, 10)), 2),
+                "p90_us": round(float(np.percentile(us, 90)), 2),
+                "gbs_at_median": round((disp_b0 + comb_b0) / (np.median(us) * 1e-6) / 1e9, 1),
+                "steps": args.cold_steps,
+                "flush": "1 GiB write before each step, untimed"}
+
     lay_ms = 0.0 if args.ll else per_launch_ms(do_layout)
     dis_ms = per_launch_ms(do_dispatch)
     com_ms = per_launch_ms(do_combine)
@@ -461,6 +496,13 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
     }
+    if cold:
+        result["cold"] = cold
+    props = torch.cuda.get_device_properties(0)
+    result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                        "compute_units": props.multi_processor_count,
+                        "memory_gib": round(props.total_memory / 2 ** 30, 1),
+                        "hip": torch.version.hip, "torch": torch.__version__}
     if overlap:
         result["overlap"] = overlap
     if not args.no_ceiling:
