@@ -282,8 +282,11 @@ def main():
                     help="also time the K steps concurrently with K bf16 GEMMs "
                          "[M,K]x[K,N] on a second stream (e.g. 8192x7168x4096)")
     ap.add_argument("--cold-steps", type=int, default=50, metavar="C",
-                    help="also time C single steps, each after an untimed 1 GiB write that "
-                         "evicts L2 and the Infinity Cache (0 skips)")
+                    help="also time C single steps, each after an untimed pass over 1 GiB "
+                         "that evicts L2 and the Infinity Cache (0 skips)")
+    ap.add_argument("--cold-flush", choices=("read", "write"), default="read",
+                    help="the eviction pass: read (leaves clean lines) or write (leaves "
+                         "dirty lines that are written back during the step)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying a HIP graph")
     ap.add_argument("--summarize", action="store_true",
@@ -417,16 +420,19 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    # Cold-cache steps: one step at a time, each after an untimed 1 GiB write
-    # (more than the 256 MB Infinity Cache plus the L2s), timed by events on
-    # the launch stream; median and spread over the steps.
+    # Cold-cache steps: one step at a time, each after an untimed pass over
+    # 1 GiB (more than the 256 MB Infinity Cache plus the L2s), timed by events
+    # on the launch stream; median and spread over the steps.
     cold = None
     if args.cold_steps > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.cold_steps)]
         for i, (a, b) in enumerate(evs):
-            flush.fill_(i & 0xFF)
+            if args.cold_flush == "read":
+                flush.sum(dtype=torch.int64)
+            else:
+                flush.fill_(i)
             a.record()
             step()
             b.record()
@@ -439,7 +445,7 @@ def main():
                 "p90_us": round(float(np.percentile(us, 90)), 2),
                 "gbs_at_median": round((disp_b0 + comb_b0) / (np.median(us) * 1e-6) / 1e9, 1),
                 "steps": args.cold_steps,
-                "flush": "1 GiB write before each step, untimed"}
+                "flush": f"1 GiB {args.cold_flush} before each step, untimed"}
 
     lay_ms = 0.0 if args.ll else per_launch_ms(do_layout)
     dis_ms = per_launch_ms(do_dispatch)
