@@ -156,7 +156,7 @@ def summarize(args):
     stats = _csv_rows(os.path.join(args.trace_dir, "run_kernel_stats.csv"))
     lines = [f"# rocprofv3 kernel statistics: {w.desc}",
              f"# command: cd /tmp && rocprofv3 --kernel-trace --stats -T -f csv -d <out> -o run -- "
-             f"{cmd_base} --steps 20 --warmup 5 --cpu-seconds 0 --no-ceiling",
+             f"{cmd_base} --steps 20 --warmup 5 --cpu-seconds 0 --no-ceiling --cold-steps 0",
              f"# kernel source sha256 (comments and blank space stripped): {source_sha()}",
              f"{'kernel':28s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
     for r in stats:
@@ -191,9 +191,9 @@ def summarize(args):
         wb = write[kname] * w_scale * 1024
         txt = [f"# HBM byte audit (rocprofv3 --pmc), {kname}, {w.desc}",
                f"# commands: cd /tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv -d <out> -o run -- "
-               f"{cmd_base} --steps 3 --warmup 1 --cpu-seconds 0",
+               f"{cmd_base} --steps 3 --warmup 1 --cpu-seconds 0 --cold-steps 0",
                f"#           cd /tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv -d <out> -o run -- "
-               f"{cmd_base} --steps 3 --warmup 1 --cpu-seconds 0",
+               f"{cmd_base} --steps 3 --warmup 1 --cpu-seconds 0 --cold-steps 0",
                "# scale: counter KiB of the 1 GiB copy kernel in the same run -> bytes",
                "# source_sha256: ep_get.hip with comments and blank space stripped",
                f"kernel: {kname}",
