@@ -60,9 +60,18 @@ class EPError(RuntimeError):
         self.code = code
 
 
+class LLArgs(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("x_scales", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
+                ("recv_count", ctypes.c_void_p), ("slot_of", ctypes.c_void_p),
+                ("flags", ctypes.c_void_p), ("recv_x", ctypes.c_void_p),
+                ("recv_scales", ctypes.c_void_p), ("recv_src_idx", ctypes.c_void_p),
+                ("recv_topk_weights", ctypes.c_void_p), ("cumulative_recv_stats", ctypes.c_void_p)]
+
+
 EXPORTS = ("ep_recv_capacity", "ep_workspace_bytes", "ep_get_layout", "ep_dispatch",
            "ep_dispatch_ex", "ep_combine", "ep_layout_error", "ep_status_str", "ep_ll_capacity",
-           "ep_ll_dispatch")
+           "ep_ll_dispatch", "ep_ll_dispatch_ex")
 EP_LAYOUT_ERR_OVERFLOW = 2
 
 
@@ -109,6 +118,8 @@ def load(path):
     L.ep_ll_capacity.argtypes = [P, ctypes.c_int32]
     L.ep_ll_dispatch.restype = ctypes.c_int
     L.ep_ll_dispatch.argtypes = [P, ctypes.c_int32] + [vp] * 10 + [vp]
+    L.ep_ll_dispatch_ex.restype = ctypes.c_int
+    L.ep_ll_dispatch_ex.argtypes = [P, ctypes.c_int32, ctypes.POINTER(LLArgs), vp]
     return L
 
 
@@ -377,11 +388,14 @@ def alloc_ll(num_tokens, num_topk, num_experts, num_ranks, max_tokens_per_rank, 
 
 
 def ll_dispatch(x, topk_idx, topk_weights, num_experts, num_ranks, max_tokens_per_rank,
-                use_fp8=False, out=None, with_meta=True):
-    """Routing and payload in one launch (see ep_ll_dispatch).
+                use_fp8=False, out=None, with_meta=True, x_scales=None, cumulative_stats=None):
+    """Routing and payload in one launch (see ep_ll_dispatch / ep_ll_dispatch_ex).
 
     Returns (layout, (recv_x, recv_scales, recv_src_idx, recv_topk_weights)).
-    ``out`` is a pair from alloc_ll for allocation-free calls."""
+    ``out`` is a pair from alloc_ll for allocation-free calls.  ``x_scales``
+    [N, H/128] fp32 makes ``x`` pre-quantised float8_e4m3fn codes (needs
+    use_fp8); ``cumulative_stats`` ([E] int64) gets the rows each expert
+    received added."""
     import torch
     N, H = x.shape
     K = topk_idx.shape[1]
@@ -391,7 +405,15 @@ def ll_dispatch(x, topk_idx, topk_weights, num_experts, num_ranks, max_tokens_pe
     if (lay.num_tokens, lay.num_topk, lay.num_experts, lay.num_ranks,
             lay.max_tokens_per_rank) != (N, K, num_experts, num_ranks, max_tokens_per_rank):
         raise ValueError("ll_dispatch: `out` was allocated for another problem")
-    _need(x, torch.bfloat16, (N, H), "x")
+    if x_scales is not None:
+        if not use_fp8:
+            raise ValueError("ll_dispatch: pre-quantised x needs use_fp8=True")
+        _need(x, torch.float8_e4m3fn, (N, H), "x")
+        _need(x_scales, torch.float32, (N, H // 128), "x_scales")
+    else:
+        _need(x, torch.bfloat16, (N, H), "x")
+    if cumulative_stats is not None:
+        _need(cumulative_stats, torch.int64, (num_experts,), "cumulative_stats")
     nb = _idx_bytes(topk_idx)
     _need(topk_idx, topk_idx.dtype, (N, K), "topk_idx")
     recv_x, scales, src, rw = recv
@@ -403,10 +425,30 @@ def ll_dispatch(x, topk_idx, topk_weights, num_experts, num_ranks, max_tokens_pe
         _need(rw, torch.float32, (lay.capacity,), "recv_topk_weights")
         _need(topk_weights, torch.float32, (N, K), "topk_weights")
     p = problem(N, H, K, num_experts, num_ranks, 1, use_fp8, nb)
-    rc = lib().ep_ll_dispatch(ctypes.byref(p), int(max_tokens_per_rank), _ptr(topk_idx), _ptr(x),
-                              _ptr(topk_weights if with_meta else None), _ptr(lay.recv_count),
-                              _ptr(lay.slot_of), _ptr(lay.flags), _ptr(recv_x),
-                              _ptr(scales if use_fp8 else None), _ptr(src if with_meta else None),
-                              _ptr(rw if with_meta else None), _stream())
-    _check("ep_ll_dispatch", rc)
+    if x_scales is None and cumulative_stats is None:
+        rc = lib().ep_ll_dispatch(ctypes.byref(p), int(max_tokens_per_rank), _ptr(topk_idx),
+                                  _ptr(x), _ptr(topk_weights if with_meta else None),
+                                  _ptr(lay.recv_count), _ptr(lay.slot_of), _ptr(lay.flags),
+                                  _ptr(recv_x), _ptr(scales if use_fp8 else None),
+                                  _ptr(src if with_meta else None),
+                                  _ptr(rw if with_meta else None), _stream())
+        _check("ep_ll_dispatch", rc)
+    else:
+        a = LLArgs()
+        a.topk_idx = topk_idx.data_ptr()
+        a.x = x.data_ptr()
+        a.x_scales = None if x_scales is None else x_scales.data_ptr()
+        a.topk_weights = topk_weights.data_ptr() if with_meta else None
+        a.recv_count = lay.recv_count.data_ptr()
+        a.slot_of = lay.slot_of.data_ptr()
+        a.flags = lay.flags.data_ptr()
+        a.recv_x = recv_x.data_ptr()
+        a.recv_scales = scales.data_ptr() if use_fp8 else None
+        a.recv_src_idx = src.data_ptr() if with_meta else None
+        a.recv_topk_weights = rw.data_ptr() if with_meta else None
+        a.cumulative_recv_stats = (None if cumulative_stats is None
+                                   else cumulative_stats.data_ptr())
+        _check("ep_ll_dispatch_ex", lib().ep_ll_dispatch_ex(ctypes.byref(p),
+                                                            int(max_tokens_per_rank),
+                                                            ctypes.byref(a), _stream()))
     return lay, (recv_x, scales if use_fp8 else None, src, rw)

@@ -1016,13 +1016,17 @@ __global__ __launch_bounds__(kPersistThreads) void dispatch_persist_kernel(
 constexpr int kLLThreads = 256;
 constexpr int kLLWaves = kLLThreads / 64;
 
-template <bool FP8, int NV, typename I>
+// MODE 0: bf16 rows; 1: fused e4m3 quantisation; 2: pre-quantised e4m3 codes
+// (x) and scales (xs) copied unchanged.  stats != NULL: the block (s, 0) adds
+// its source's received rows per expert (atomic integer adds, so the sum is
+// the same in any order).
+template <int MODE, int NV, typename I>
 __global__ __launch_bounds__(kLLThreads) void ll_dispatch_kernel(
-    const I* __restrict__ topk_idx, const u32x4* __restrict__ x,
+    const I* __restrict__ topk_idx, const u32x4* __restrict__ x, const float* __restrict__ xs,
     const float* __restrict__ w, int32_t* __restrict__ recv_count, int32_t* __restrict__ slot_of,
     int32_t* __restrict__ flags, u32x4* __restrict__ recv_x, float* __restrict__ recv_scales,
-    int32_t* __restrict__ recv_src, float* __restrict__ recv_w, int K, int E, int R, int T,
-    int M, int H, int Q) {
+    int32_t* __restrict__ recv_src, float* __restrict__ recv_w, int64_t* __restrict__ stats,
+    int K, int E, int R, int T, int M, int H, int Q) {
   __shared__ int sidx[kAssignTile];
   __shared__ int sslot[kAssignTile];
   __shared__ int cnt[EP_MAX_EXPERTS];
@@ -1073,7 +1077,12 @@ __global__ __launch_bounds__(kLLThreads) void ll_dispatch_kernel(
   if (myerr) atomicOr(&ferr, myerr);
   __syncthreads();
   if (q == 0) {
-    for (int e = tid; e < E; e += kLLThreads) recv_count[(int64_t)e * R + s] = min(cnt[e], M);
+    for (int e = tid; e < E; e += kLLThreads) {
+      const int got = min(cnt[e], M);
+      recv_count[(int64_t)e * R + s] = got;
+      if (stats && got)
+        atomicAdd(reinterpret_cast<unsigned long long*>(stats + e), (unsigned long long)got);
+    }
     if (tid == 0) flags[s] = ferr;
   }
   const int per = (T + Q - 1) / Q;
@@ -1082,10 +1091,14 @@ __global__ __launch_bounds__(kLLThreads) void ll_dispatch_kernel(
   for (int tl = ta + wv; tl < tb; tl += kLLWaves) {
     const int t = uniform(s * T + tl);
     const int myslot = (lane < K) ? sslot[tl * K + lane] : -1;
-    if constexpr (FP8)
+    if constexpr (MODE == 1) {
       quant_row_fp8<NV>(x + (int64_t)t * (H >> 3), recv_x, recv_scales, myslot, K, H, lane);
-    else
+    } else if constexpr (MODE == 2) {
+      copy_row<64, NV>(x + (int64_t)t * (H >> 4), recv_x, myslot, K, H >> 4, lane);
+      copy_scales(xs, t, H >> 7, recv_scales, myslot, K, lane);
+    } else {
       copy_row<64, NV>(x + (int64_t)t * (H >> 3), recv_x, myslot, K, H >> 3, lane);
+    }
     write_meta(t, K, lane, myslot, w, recv_src, recv_w);
   }
 }
@@ -1490,19 +1503,20 @@ void launch_combine(int q, int N, hipStream_t st, const void* eo, const int32_t*
 #undef EP_CQ
 }
 
-template <bool FP8, int NV>
-void launch_ll(int grid, size_t lds, hipStream_t st, int idx_bytes, const void* idx,
-               const void* x, const float* w, int32_t* recv_count, int32_t* slot_of,
-               int32_t* flags, void* recv_x, float* recv_scales, int32_t* recv_src,
-               float* recv_w, int K, int E, int R, int T, int M, int H, int Q) {
-  if (idx_bytes == 8)
-    ll_dispatch_kernel<FP8, NV, int64_t><<<grid, kLLThreads, lds, st>>>(
-        (const int64_t*)idx, (const u32x4*)x, w, recv_count, slot_of, flags, (u32x4*)recv_x,
-        recv_scales, recv_src, recv_w, K, E, R, T, M, H, Q);
+template <int MODE, int NV>
+void launch_ll(int grid, size_t lds, hipStream_t st, const ep_problem_t* p,
+               const ep_ll_args_t* a, int T, int M, int Q) {
+  const int K = p->num_topk, E = p->num_experts, R = p->num_ranks, H = p->hidden;
+  if (p->topk_idx_bytes == 8)
+    ll_dispatch_kernel<MODE, NV, int64_t><<<grid, kLLThreads, lds, st>>>(
+        (const int64_t*)a->topk_idx, (const u32x4*)a->x, a->x_scales, a->topk_weights,
+        a->recv_count, a->slot_of, a->flags, (u32x4*)a->recv_x, a->recv_scales, a->recv_src_idx,
+        a->recv_topk_weights, a->cumulative_recv_stats, K, E, R, T, M, H, Q);
   else
-    ll_dispatch_kernel<FP8, NV, int32_t><<<grid, kLLThreads, lds, st>>>(
-        (const int32_t*)idx, (const u32x4*)x, w, recv_count, slot_of, flags, (u32x4*)recv_x,
-        recv_scales, recv_src, recv_w, K, E, R, T, M, H, Q);
+    ll_dispatch_kernel<MODE, NV, int32_t><<<grid, kLLThreads, lds, st>>>(
+        (const int32_t*)a->topk_idx, (const u32x4*)a->x, a->x_scales, a->topk_weights,
+        a->recv_count, a->slot_of, a->flags, (u32x4*)a->recv_x, a->recv_scales, a->recv_src_idx,
+        a->recv_topk_weights, a->cumulative_recv_stats, K, E, R, T, M, H, Q);
 }
 
 }  // namespace
@@ -1730,56 +1744,81 @@ int64_t ep_ll_capacity(const ep_problem_t* p, int32_t max_tokens_per_rank) {
   return cap > INT32_MAX ? -1 : cap;
 }
 
-int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const void* topk_idx,
-                   const void* x, const float* topk_weights, int32_t* recv_count,
-                   int32_t* slot_of, int32_t* flags, void* recv_x, float* recv_scales,
-                   int32_t* recv_src_idx, float* recv_topk_weights, void* stream) {
+int ep_ll_dispatch_ex(const ep_problem_t* p, int32_t max_tokens_per_rank, const ep_ll_args_t* a,
+                      void* stream) {
   int rc = validate_payload(p);
   if (rc != EP_OK) return rc;
+  if (!a) return EP_ERR_INVALID_ARG;
   const int N = p->num_tokens, K = p->num_topk, E = p->num_experts, R = p->num_ranks;
   const int M = max_tokens_per_rank, H = p->hidden;
   if (ep_ll_capacity(p, M) < 0) return EP_ERR_INVALID_ARG;
   const int T = N / R;
+  const bool prequant = a->x_scales != nullptr;
   if ((int64_t)T * K > kAssignTile) return EP_ERR_INVALID_ARG;
-  if (!recv_count || !flags) return EP_ERR_INVALID_ARG;
-  if (N > 0 && (!topk_idx || !x || !slot_of || !recv_x)) return EP_ERR_INVALID_ARG;
-  if (p->use_fp8 && N > 0 && !recv_scales) return EP_ERR_INVALID_ARG;
-  if (recv_topk_weights && N > 0 && !topk_weights) return EP_ERR_INVALID_ARG;
+  if (!a->recv_count || !a->flags) return EP_ERR_INVALID_ARG;
+  if (prequant && !p->use_fp8) return EP_ERR_INVALID_ARG;
+  if (N > 0 && (!a->topk_idx || !a->x || !a->slot_of || !a->recv_x)) return EP_ERR_INVALID_ARG;
+  if (p->use_fp8 && N > 0 && !a->recv_scales) return EP_ERR_INVALID_ARG;
+  if (a->recv_topk_weights && N > 0 && !a->topk_weights) return EP_ERR_INVALID_ARG;
   rc = check_device();
   if (rc != EP_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   if (N == 0) {
-    ll_empty_kernel<<<1, kThreads, 0, st>>>(recv_count, flags, E, R);
+    ll_empty_kernel<<<1, kThreads, 0, st>>>(a->recv_count, a->flags, E, R);
     return check_launch("ll_empty");
   }
   const int Q = (T + kLLWaves - 1) / kLLWaves;
   const int grid = R * Q;
   const size_t lds = sizeof(unsigned long long) * kLLWaves * (size_t)E;
-  EP_LOG("ll dispatch N=%d H=%d K=%d E=%d R=%d M=%d fp8=%d: blocks=%d", N, H, K, E, R, M,
-         p->use_fp8, grid);
-#define EP_LL(FP, NV)                                                                        \
-  launch_ll<FP, NV>(grid, lds, st, p->topk_idx_bytes, topk_idx, x, topk_weights, recv_count,  \
-                    slot_of, flags, recv_x, recv_scales, recv_src_idx, recv_topk_weights, K, E, \
-                    R, T, M, H, Q)
-  if (!p->use_fp8) {
+  const int mode = prequant ? 2 : (p->use_fp8 ? 1 : 0);
+  EP_LOG("ll dispatch N=%d H=%d K=%d E=%d R=%d M=%d mode=%d stats=%d: blocks=%d", N, H, K, E, R,
+         M, mode, a->cumulative_recv_stats != nullptr, grid);
+#define EP_LL(MD, NV) launch_ll<MD, NV>(grid, lds, st, p, a, T, M, Q)
+  if (mode == 0) {
     const int q = (H / 8 + 63) / 64;
-    if (q <= 1) EP_LL(false, 1);
-    else if (q <= 2) EP_LL(false, 2);
-    else if (q <= 4) EP_LL(false, 4);
-    else if (q <= 7) EP_LL(false, 7);
-    else if (q <= 8) EP_LL(false, 8);
-    else if (q <= 14) EP_LL(false, 14);
-    else EP_LL(false, 16);
-  } else {
+    if (q <= 1) EP_LL(0, 1);
+    else if (q <= 2) EP_LL(0, 2);
+    else if (q <= 4) EP_LL(0, 4);
+    else if (q <= 7) EP_LL(0, 7);
+    else if (q <= 8) EP_LL(0, 8);
+    else if (q <= 14) EP_LL(0, 14);
+    else EP_LL(0, 16);
+  } else if (mode == 1) {
     const int q = (H + 1023) / 1024;
-    if (q <= 1) EP_LL(true, 1);
-    else if (q <= 2) EP_LL(true, 2);
-    else if (q <= 4) EP_LL(true, 4);
-    else if (q <= 7) EP_LL(true, 7);
-    else EP_LL(true, 8);
+    if (q <= 1) EP_LL(1, 1);
+    else if (q <= 2) EP_LL(1, 2);
+    else if (q <= 4) EP_LL(1, 4);
+    else if (q <= 7) EP_LL(1, 7);
+    else EP_LL(1, 8);
+  } else {
+    const int q = (H / 16 + 63) / 64;
+    if (q <= 1) EP_LL(2, 1);
+    else if (q <= 2) EP_LL(2, 2);
+    else if (q <= 4) EP_LL(2, 4);
+    else if (q <= 7) EP_LL(2, 7);
+    else if (q <= 8) EP_LL(2, 8);
+    else EP_LL(2, 16);
   }
 #undef EP_LL
   return check_launch("ll_dispatch");
+}
+
+int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const void* topk_idx,
+                   const void* x, const float* topk_weights, int32_t* recv_count,
+                   int32_t* slot_of, int32_t* flags, void* recv_x, float* recv_scales,
+                   int32_t* recv_src_idx, float* recv_topk_weights, void* stream) {
+  ep_ll_args_t a{};
+  a.topk_idx = topk_idx;
+  a.x = x;
+  a.topk_weights = topk_weights;
+  a.recv_count = recv_count;
+  a.slot_of = slot_of;
+  a.flags = flags;
+  a.recv_x = recv_x;
+  a.recv_scales = recv_scales;
+  a.recv_src_idx = recv_src_idx;
+  a.recv_topk_weights = recv_topk_weights;
+  return ep_ll_dispatch_ex(p, max_tokens_per_rank, &a, stream);
 }
 
 int ep_layout_error(const void* workspace, int32_t* flags, void* stream) {

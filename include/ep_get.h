@@ -247,6 +247,33 @@ int ep_ll_dispatch(const ep_problem_t* p, int32_t max_tokens_per_rank, const voi
                    int32_t* slot_of, int32_t* flags, void* recv_x, float* recv_scales,
                    int32_t* recv_src_idx, float* recv_topk_weights, void* stream);
 
+/* Low-latency dispatch with the options of DeepEP's V2 dispatch that apply to
+ * fixed sub-blocks (DeepEP book ch.1 sec. 1.1): every field means what the
+ * argument of the same name of ep_ll_dispatch means, plus
+ *   x_scales    NULL: x is bf16 (quantised when use_fp8).  Otherwise x holds
+ *               pre-quantised E4M3FN codes [N][H] and x_scales their fp32
+ *               scales [N][H/128], copied unchanged (requires use_fp8).
+ *   cumulative_recv_stats  [E] int64 or NULL: stats[e] += sum over sources s
+ *               of recv_count[e][s] (rows actually placed), once per call.
+ * Zero padding is not offered here: the unused rows of the sub-blocks are
+ * E*R*M - placed rows, usually most of the buffer. */
+typedef struct ep_ll_args {
+  const void* topk_idx;
+  const void* x;
+  const float* x_scales;
+  const float* topk_weights;
+  int32_t* recv_count;
+  int32_t* slot_of;
+  int32_t* flags;
+  void* recv_x;
+  float* recv_scales;
+  int32_t* recv_src_idx;
+  float* recv_topk_weights;
+  int64_t* cumulative_recv_stats;
+} ep_ll_args_t;
+int ep_ll_dispatch_ex(const ep_problem_t* p, int32_t max_tokens_per_rank, const ep_ll_args_t* args,
+                      void* stream);
+
 /* SYNCHRONOUS debug query: waits for `stream`, then stores the error word of
  * the last ep_get_layout that used `workspace` into *flags (host pointer).
  * Bits: EP_LAYOUT_ERR_INDEX. */

@@ -185,3 +185,21 @@ def test_cu_budget_validation():
     assert L.ep_combine(ctypes.byref(p), None, None, None, None, 0, None) == 1
     p = _p(cu_budget=4)
     assert ep.lib().ep_recv_capacity(ctypes.byref(p)) == 32
+
+
+def test_ll_dispatch_ex_validation():
+    L = ep.lib()
+    fake = ctypes.c_void_p(256).value
+    p = _p()
+    assert L.ep_ll_dispatch_ex(ctypes.byref(p), 8, None, None) == 1
+    a = ep.LLArgs()
+    for f in ("topk_idx", "x", "topk_weights", "recv_count", "slot_of", "flags", "recv_x",
+              "recv_src_idx", "recv_topk_weights"):
+        setattr(a, f, fake)
+    a.x_scales = fake                  # pre-quantised input without use_fp8
+    assert L.ep_ll_dispatch_ex(ctypes.byref(p), 8, ctypes.byref(a), None) == 1
+    p8 = _p(use_fp8=True)              # fp8 without a scale buffer
+    assert L.ep_ll_dispatch_ex(ctypes.byref(p8), 8, ctypes.byref(a), None) == 1
+    a.x_scales = None
+    a.recv_count = None                # the mask is required
+    assert L.ep_ll_dispatch_ex(ctypes.byref(p), 8, ctypes.byref(a), None) == 1

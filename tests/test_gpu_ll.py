@@ -93,3 +93,40 @@ def test_ll_small_and_empty():
         x = torch.from_numpy(rng.standard_normal((N, H), dtype=np.float32)).to(torch.bfloat16) \
             .view(torch.int16).numpy().view(np.uint16)
         run_ll(idx, x, rng.random((N, K), dtype=np.float32), E, R, M, fp8)
+
+
+@pytest.mark.parametrize("M", [64, 3])
+def test_ll_prequantized_and_stats(M):
+    """Pre-quantised e4m3 input copied unchanged into the sub-blocks, and the
+    running per-expert counts growing by the placed rows once per call (M = 3
+    overflows many sub-blocks, so placed rows < routed pairs)."""
+    w = wl.CONFIGS[2]
+    inp = wl.make_inputs(w, 1)
+    rng = np.random.default_rng(17)
+    N, H, K, E, R = w.N, w.H, w.K, w.E, w.R
+    codes = rng.integers(0, 256, size=(N, H), dtype=np.uint8)
+    scales = rng.standard_normal((N, H // 128)).astype(np.float32)
+    say(f"ll pre-quantised + stats {w.desc} M={M}")
+    stats = torch.full((E,), 5, dtype=torch.int64, device="cuda")
+    xq = torch.from_numpy(codes).cuda().view(torch.float8_e4m3fn)
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    wts = torch.from_numpy(inp["topk_weights"]).cuda()
+    for _ in range(2):
+        lay, (rx, rs, src, _) = ep.ll_dispatch(xq, idx, wts, E, R, M, True,
+                                               x_scales=torch.from_numpy(scales).cuda(),
+                                               cumulative_stats=stats)
+    torch.cuda.synchronize()
+    ref = oracle.ll_layout(inp["topk_idx"], E, R, M)
+    np.testing.assert_array_equal(lay.slot_of.cpu().numpy(), ref["slot_of"])
+    np.testing.assert_array_equal(lay.recv_count.cpu().numpy(), ref["recv_count"])
+    t, k = np.nonzero(ref["slot_of"] >= 0)
+    sl = torch.from_numpy(ref["slot_of"][t, k].astype(np.int64)).cuda()
+    np.testing.assert_array_equal(host_u8(rx.view(torch.uint8).index_select(0, sl)), codes[t])
+    np.testing.assert_array_equal(rs.index_select(0, sl).cpu().numpy().view(np.uint32),
+                                  scales[t].view(np.uint32))
+    np.testing.assert_array_equal(src.index_select(0, sl).cpu().numpy(), t)
+    want = np.full(E, 5, np.int64)
+    per_expert = ref["recv_count"].sum(axis=1).astype(np.int32)
+    oracle.accumulate_stats(per_expert, want)
+    oracle.accumulate_stats(per_expert, want)
+    np.testing.assert_array_equal(stats.cpu().numpy(), want)
