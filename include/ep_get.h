@@ -38,8 +38,9 @@
  *     combine calls with the same routing.
  *   - Return values: EP_OK, or an EP_ERR_* code.  Argument checks run on the
  *     host only and never synchronise.  No C++ exception crosses this ABI.
- *   - The library keeps no mutable global state besides a per-device cache of
- *     the architecture check; concurrent calls need distinct workspaces.
+ *   - The library keeps no mutable global state besides per-device caches of
+ *     the architecture check and of the LDS size; concurrent calls need
+ *     distinct workspaces.
  *   - Set EP_GET_LOG=1 in the environment to print launch shapes to stderr.
  */
 #ifndef EP_GET_H
