@@ -1275,6 +1275,59 @@ __global__ __launch_bounds__(kPersistThreads) void combine_persist_kernel(
   }
 }
 
+// Combine under a CU budget for rows of at most 16 wavefronts (H8 <= 1024)
+// and K <= 8: one workgroup of 64*Q threads per CU takes tokens
+// t = blockIdx.x, t + gridDim.x, ...; each thread owns one 16-byte chunk
+// column of the row, as in combine_kernel, and gathers the next token's K
+// rows while it reduces the current one, so two tokens' rows are in flight.
+template <int Q>
+__global__ __launch_bounds__(64 * Q) void combine_persist_tok_kernel(
+    const u32x4* __restrict__ eo, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ w, u32x4* __restrict__ y, int N, int K, int H8, int64_t cap) {
+  extern __shared__ int lds[];  // only reserves the CU
+  if (N < 0) lds[threadIdx.x] = 0;
+  constexpr int TPT = 64 * Q;
+  const int vl = threadIdx.x, lane = vl & 63;
+  const int G = gridDim.x;
+  int t = blockIdx.x;
+  if (t >= N) return;
+  u32x4 va[8][1], vb[8][1];
+  int sa = load_slot(slot_of, t, K, lane, cap);
+  float wa = (lane < K) ? w[(int64_t)t * K + lane] : 0.0f;
+  combine_load8<TPT, 1>(va, eo, sa, K, 0, vl, H8);
+  while (true) {
+    // token t is in va; fetch t + G into vb, reduce t
+    const int tb = t + G;
+    int sb = -1;
+    float wb = 0.0f;
+    if (tb < N) {
+      sb = load_slot(slot_of, tb, K, lane, cap);
+      wb = (lane < K) ? w[(int64_t)tb * K + lane] : 0.0f;
+      combine_load8<TPT, 1>(vb, eo, sb, K, 0, vl, H8);
+    }
+    combine_pass8<TPT, 1>(va, sa, wa, K, y + (int64_t)t * H8, 0, vl, H8);
+    if (tb >= N) break;
+    // token tb is in vb; fetch tb + G into va, reduce tb
+    const int ta = tb + G;
+    if (ta < N) {
+      sa = load_slot(slot_of, ta, K, lane, cap);
+      wa = (lane < K) ? w[(int64_t)ta * K + lane] : 0.0f;
+      combine_load8<TPT, 1>(va, eo, sa, K, 0, vl, H8);
+    }
+    combine_pass8<TPT, 1>(vb, sb, wb, K, y + (int64_t)tb * H8, 0, vl, H8);
+    if (ta >= N) break;
+    t = ta;
+  }
+}
+
+template <int Q>
+void launch_combine_persist_tok(int grid, size_t lds, hipStream_t st, const void* eo,
+                                const int32_t* slot_of, const float* w, void* y, int N, int K,
+                                int H8, int64_t cap) {
+  combine_persist_tok_kernel<Q><<<grid, 64 * Q, lds, st>>>((const u32x4*)eo, slot_of, w,
+                                                           (u32x4*)y, N, K, H8, cap);
+}
+
 // ---------------------------------------------------------------- host side
 bool log_on() {
   static int v = -1;
@@ -1718,6 +1771,34 @@ int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slo
   hipStream_t st = (hipStream_t)stream;
   const int H8 = p->hidden / 8;
   const int q = (H8 + 63) / 64;  // wavefronts for one chunk per thread
+  if (p->cu_budget > 0 && p->num_topk <= 8 && q <= 16) {
+    const int pg = N < p->cu_budget ? N : p->cu_budget;
+    const size_t lds = persist_lds();
+    EP_LOG("combine (CU budget %d, token pipeline) N=%d H=%d K=%d: workgroups=%d lds=%zu",
+           p->cu_budget, N, p->hidden, p->num_topk, pg, lds);
+    if (lds < 4 * (2 * (size_t)EP_MAX_EXPERTS + 1)) return EP_ERR_HIP;
+#define EP_CPT(QQ) launch_combine_persist_tok<QQ>(pg, lds, st, expert_out, slot_of, topk_weights, \
+                                                  y, N, p->num_topk, H8, recv_capacity)
+    switch (q) {
+      case 1: EP_CPT(1); break;
+      case 2: EP_CPT(2); break;
+      case 3:
+      case 4: EP_CPT(4); break;
+      case 5:
+      case 6:
+      case 7: EP_CPT(7); break;
+      case 8: EP_CPT(8); break;
+      case 9:
+      case 10:
+      case 11:
+      case 12:
+      case 13:
+      case 14: EP_CPT(14); break;
+      default: EP_CPT(16); break;
+    }
+#undef EP_CPT
+    return check_launch("combine_persist_tok");
+  }
   if (p->cu_budget > 0) {
     constexpr int nv = kCombinePersistNV;
     const int64_t items = (int64_t)N * ((H8 + 64 * nv - 1) / (64 * nv));
