@@ -11,7 +11,7 @@ import combine_ep_get_amd as ep
 import oracle
 from combine_ep_get_amd import workloads as wl
 
-from .gpu_util import check_combine, dev_bf16, host_u16, say
+from .gpu_util import check_combine, dev_bf16, say
 
 pytestmark = pytest.mark.gpu
 

@@ -3,7 +3,6 @@
 on the CPU and checks that at least one of the oracle's pins now fails.  This is
 the evidence that the pins constrain every part of the oracle.
 """
-import os
 import shutil
 import subprocess
 
