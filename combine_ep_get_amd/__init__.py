@@ -452,3 +452,18 @@ def ll_dispatch(x, topk_idx, topk_weights, num_experts, num_ranks, max_tokens_pe
                                                             int(max_tokens_per_rank),
                                                             ctypes.byref(a), _stream()))
     return lay, (recv_x, scales if use_fp8 else None, src, rw)
+
+
+# The C entry points' own names, for callers who read include/ep_get.h: each
+# is the function above that marshals that entry point's arguments (the
+# *_ex variants are reached through dispatch's / ll_dispatch's options).
+ep_recv_capacity = recv_capacity
+ep_workspace_bytes = workspace_bytes
+ep_get_layout = get_layout
+ep_dispatch = dispatch
+ep_dispatch_ex = dispatch
+ep_combine = combine
+ep_layout_error = layout_error
+ep_ll_capacity = ll_capacity
+ep_ll_dispatch = ll_dispatch
+ep_ll_dispatch_ex = ll_dispatch

@@ -203,3 +203,10 @@ def test_ll_dispatch_ex_validation():
     a.x_scales = None
     a.recv_count = None                # the mask is required
     assert L.ep_ll_dispatch_ex(ctypes.byref(p), 8, ctypes.byref(a), None) == 1
+
+
+def test_binding_offers_every_entry_point_by_its_c_name():
+    for fn in declared_functions():
+        if fn == "ep_status_str":
+            continue   # raised as the message of EPError
+        assert callable(getattr(ep, fn, None)), fn
