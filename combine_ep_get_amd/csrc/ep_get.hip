@@ -1009,10 +1009,15 @@ __global__ __launch_bounds__(kPersistThreads) void dispatch_persist_kernel(
 // source s routed to e goes to slot (e*R + s)*M + j, j being its rank among
 // source s's pairs routed to e in (token, k) order.  A slot therefore depends
 // only on the pairs of its own source, and no device-wide scan is needed.
-// Block (s, q) ranks all pairs of source s (redundantly with the source's
-// other blocks; T*K <= kAssignTile) and then moves the rows of its own
-// kLLWaves tokens, one wavefront per token.  Pairs beyond M in a sub-block
-// get no slot and set EP_LAYOUT_ERR_OVERFLOW in the source's flags.
+// Block (s, q) moves the rows of its own kLLWaves tokens, one wavefront per
+// token.  The rank of one of its pairs is the number of earlier pairs of the
+// source routed to the same expert: pairs of earlier tokens are counted with
+// one pass of LDS atomic adds (a count, so their order does not matter), and
+// the block's own pairs (at most kLLWaves*K <= 128) are ranked in one round
+// of per-wavefront 64-bit masks and popcounts.  Block (s, 0) also counts all
+// of the source's pairs, which gives recv_count, the flags and the running
+// statistics.  Pairs beyond M in a sub-block get no slot and set
+// EP_LAYOUT_ERR_OVERFLOW in the source's flags.
 constexpr int kLLThreads = 256;
 constexpr int kLLWaves = kLLThreads / 64;
 
@@ -1028,16 +1033,38 @@ __global__ __launch_bounds__(kLLThreads) void ll_dispatch_kernel(
     int32_t* __restrict__ recv_src, float* __restrict__ recv_w, int64_t* __restrict__ stats,
     int K, int E, int R, int T, int M, int H, int Q) {
   __shared__ int sidx[kAssignTile];
-  __shared__ int sslot[kAssignTile];
-  __shared__ int cnt[EP_MAX_EXPERTS];
+  __shared__ int sslot[kLLWaves * EP_MAX_TOPK];
+  __shared__ int cnt[EP_MAX_EXPERTS];   // pairs of earlier tokens (q > 0) or all pairs (q == 0)
   __shared__ int ferr;
   extern __shared__ unsigned long long masks[];  // [kLLWaves][E]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int s = blockIdx.x / Q, q = blockIdx.x % Q;
   const int np = T * K;
   const int64_t p0 = (int64_t)s * T * K;
+  const int per = (T + Q - 1) / Q;
+  const int ta = min(T, q * per), tb = min(T, ta + per);
+  const int own0 = ta * K, nown = (tb - ta) * K;
+  // pairs this block reads: all of the source for q == 0, else those up to its last token
+  const int nread = (q == 0) ? np : tb * K;
   int iv[kAssignTile / kLLThreads];
-  load_idx<kLLThreads, kAssignTile>(iv, topk_idx + p0, np);
+  if (nread > 0) load_idx<kLLThreads, kAssignTile>(iv, topk_idx + p0, nread);
+  // A copied row (bf16 or pre-quantised codes) does not depend on the routing:
+  // when it fits one pass, each wavefront requests its token's row now, so
+  // the load latency overlaps the ranking below (per <= kLLWaves: at most one
+  // token per wavefront).
+  constexpr bool kCopy = (MODE != 1);
+  const int rowc = (MODE == 2) ? (H >> 4) : (H >> 3);
+  const bool prefetch = kCopy && rowc <= 64 * NV;
+  const int tl0 = ta + wv;
+  u32x4 row[NV];
+  if (prefetch && tl0 < tb) {
+    const u32x4* src = x + (int64_t)(s * T + tl0) * rowc;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int c = i * 64 + lane;
+      if (c < rowc) row[i] = ld16<EP_DISPATCH_NT_LOAD>(src + c);
+    }
+  }
   for (int e = tid; e < E; e += kLLThreads) {
     cnt[e] = 0;
 #pragma unroll
@@ -1045,35 +1072,20 @@ __global__ __launch_bounds__(kLLThreads) void ll_dispatch_kernel(
   }
   if (tid == 0) ferr = 0;
   __syncthreads();
-  store_idx<kLLThreads, kAssignTile>(sidx, iv, np);
+  if (nread > 0) store_idx<kLLThreads, kAssignTile>(sidx, iv, nread);
   __syncthreads();
-  const unsigned long long below = (1ull << lane) - 1ull;
+  // counts: pairs before the block's own tokens (q > 0), every pair (q == 0)
+  const int ncount = (q == 0) ? np : own0;
   int myerr = 0;
-  for (int r0 = 0; r0 < np; r0 += kLLThreads) {
-    const int p = r0 + tid;
-    const int e = (p < np) ? sidx[p] : -1;
-    const bool ok = (e >= 0 && e < E);
-    if (p < np && !ok && e != -1) myerr |= EP_LAYOUT_ERR_INDEX;
-    if (ok) atomicOr(&masks[wv * E + e], 1ull << lane);
-    __syncthreads();
-    int slot = -1;
-    unsigned long long m = 0;
-    if (ok) {
-      m = masks[wv * E + e];
-      int pw = 0;
-      for (int w2 = 0; w2 < wv; w2++) pw += __popcll(masks[w2 * E + e]);
-      const int j = cnt[e] + pw + __popcll(m & below);
-      if (j < M) slot = (e * R + s) * M + j;
-      else myerr |= EP_LAYOUT_ERR_OVERFLOW;
-    }
-    __syncthreads();
-    if (ok && (m & below) == 0ull) {
-      atomicAdd(&cnt[e], __popcll(m));
-      masks[wv * E + e] = 0ull;
-    }
-    if (p < np) sslot[p] = slot;
-    __syncthreads();
+  for (int p = tid; p < ncount; p += kLLThreads) {
+    const int e = sidx[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    else if (e != -1) myerr |= EP_LAYOUT_ERR_INDEX;
   }
+  // the block's own pairs: one round of masks (nown <= kLLThreads)
+  const int e_own = (tid < nown) ? sidx[own0 + tid] : -1;
+  const bool ok = (e_own >= 0 && e_own < E);
+  if (ok) atomicOr(&masks[wv * E + e_own], 1ull << lane);
   if (myerr) atomicOr(&ferr, myerr);
   __syncthreads();
   if (q == 0) {
@@ -1082,15 +1094,47 @@ __global__ __launch_bounds__(kLLThreads) void ll_dispatch_kernel(
       recv_count[(int64_t)e * R + s] = got;
       if (stats && got)
         atomicAdd(reinterpret_cast<unsigned long long*>(stats + e), (unsigned long long)got);
+      if (cnt[e] > M) atomicOr(&ferr, EP_LAYOUT_ERR_OVERFLOW);
     }
-    if (tid == 0) flags[s] = ferr;
   }
-  const int per = (T + Q - 1) / Q;
-  const int ta = q * per, tb = min(T, ta + per);
-  for (int i = ta * K + tid; i < tb * K; i += kLLThreads) slot_of[p0 + i] = sslot[i];
+  if (tid < nown) {
+    int slot = -1;
+    if (ok) {
+      const unsigned long long below = (1ull << lane) - 1ull;
+      int pw = 0;
+      for (int w2 = 0; w2 < wv; w2++) pw += __popcll(masks[w2 * E + e_own]);
+      // q == 0 owns the first tokens, so nothing of the source precedes them
+      const int before = (q == 0) ? 0 : cnt[e_own];
+      const int j = before + pw + __popcll(masks[wv * E + e_own] & below);
+      if (j < M) slot = (e_own * R + s) * M + j;
+    }
+    sslot[tid] = slot;
+    slot_of[p0 + own0 + tid] = slot;
+  }
+  __syncthreads();
+  if (q == 0 && tid == 0) flags[s] = ferr;
+  if (prefetch) {
+    if (tl0 < tb) {
+      const int t = uniform(s * T + tl0);
+      const int myslot = (lane < K) ? sslot[(tl0 - ta) * K + lane] : -1;
+      for (int k = 0; k < K; k++) {
+        const int sl = lane_value(myslot, k);
+        if (sl < 0) continue;
+        u32x4* dst = recv_x + (int64_t)sl * rowc;
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+          const int c = i * 64 + lane;
+          if (c < rowc) st16(dst + c, row[i]);
+        }
+      }
+      if constexpr (MODE == 2) copy_scales(xs, t, H >> 7, recv_scales, myslot, K, lane);
+      write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+    }
+    return;
+  }
   for (int tl = ta + wv; tl < tb; tl += kLLWaves) {
     const int t = uniform(s * T + tl);
-    const int myslot = (lane < K) ? sslot[tl * K + lane] : -1;
+    const int myslot = (lane < K) ? sslot[(tl - ta) * K + lane] : -1;
     if constexpr (MODE == 1) {
       quant_row_fp8<NV>(x + (int64_t)t * (H >> 3), recv_x, recv_scales, myslot, K, H, lane);
     } else if constexpr (MODE == 2) {
