@@ -300,7 +300,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (virtual EP ranks inside one GPU's "
+        print(f"bench.py: this implementation runs on one GPU only (virtual EP ranks inside one GPU's "
               f"HBM); --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 
@@ -479,7 +479,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "e4m3" if w.fp8 else "bf16",
-        "data": "synthetic (seeded numpy; see DESIGN.md input recipe)",
+        "data": "synthetic (seeded numpy draws with the workload's shapes and routing)",
         "config": {"workload": f"{w.name}: {w.N} tokens x hidden {w.H}, {w.E} experts, "
                                f"top-{w.K}, {w.R} virtual ranks, expert_alignment {w.A}, "
                                f"{'e4m3' if w.fp8 else 'bf16'} dispatch, {w.routing} routing",

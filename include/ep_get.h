@@ -61,7 +61,7 @@ enum {
   EP_ERR_UNSUPPORTED = 4  /* the current device is not gfx950                      */
 };
 
-/* Limits of this build. */
+/* Compile-time limits of the library. */
 #define EP_MAX_EXPERTS 1024
 #define EP_MAX_RANKS 256
 #define EP_MAX_TOPK 32
