@@ -148,6 +148,8 @@ int ep_get_layout(const ep_problem_t* p, const void* topk_idx,
  *   topk_weights        [N][K] fp32 gate weights (may be NULL iff
  *                       recv_topk_weights is NULL)
  *   slot_of, expert_slot_offset, num_recv_per_expert: from ep_get_layout
+ *                       (the last two are read only to tag padding slots,
+ *                       i.e. when recv_src_idx or recv_topk_weights is given)
  *   recv_x              [recv_capacity][H] bf16 (use_fp8 == 0) or E4M3FN
  *                       bytes (use_fp8 == 1); only slots that hold a pair are
  *                       written, padding rows keep their previous bytes
