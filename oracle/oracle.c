@@ -33,8 +33,10 @@
  *   "no expert" and is skipped; any other value outside [0, E) sets error bit
  *   0 and is skipped; the FP8 format is OCP E4M3FN with round-to-nearest-even
  *   and saturation to +-448; scale = amax/448 and the quantiser multiplies by
- *   448/amax (both one float32 division); amax == 0 gives scale 1 and signed
- *   zero codes; padding slots carry no payload, source index -1, weight 0.
+ *   448/amax (both one float32 division); where 448/amax overflows float32 the
+ *   group is first multiplied by 2^64 (exact), since the codes only depend on
+ *   v/amax; amax == 0 gives scale 1 and signed zero codes; padding slots carry
+ *   no payload, source index -1, weight 0.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fPIC -shared oracle.c -lm
  * (no FMA contraction: every float product and sum is rounded on its own).
@@ -289,7 +291,14 @@ void oracle_dispatch_bf16(int32_t N, int32_t K, int32_t H, const uint16_t* x,
  *   amax = max |v| over the group (v is the exact float of the bf16 value)
  *   scale = amax / 448, inv = 448 / amax (one float32 division each)
  *   q = E4M3FN(v * inv)  (one float32 multiply, then the encoder above)
- * amax == 0 gives scale 1 and +-0 codes.  Dequantisation is q * scale. */
+ * amax == 0 gives scale 1 and +-0 codes.  Dequantisation is q * scale.
+ * What the codes approximate is v * 448 / amax, which does not change when
+ * the whole group is multiplied by a power of two.  For amax below 448/FLT_MAX
+ * (about 1.3e-36) the float32 inverse overflows, so there the values and
+ * amax are first multiplied by 2^64 -- exact for every bf16 value, and it
+ * leaves the codes of any group whose inverse is finite either way unchanged
+ * -- and the codes are those of the scaled group.  The scale is still the
+ * float32 quotient amax / 448 of the group as given. */
 void oracle_quantize_row(int32_t H, const uint16_t* xrow, uint8_t* q, float* scales) {
   for (int32_t g = 0; g < H / 128; g++) {
     float amax = 0.0f;
@@ -305,9 +314,14 @@ void oracle_quantize_row(int32_t H, const uint16_t* xrow, uint8_t* q, float* sca
     }
     float scale = amax / 448.0f;
     float inv = 448.0f / amax;
+    int pre = 0; /* power of two applied to the group before the multiply */
+    if (isinf(inv)) {
+      pre = 64;
+      inv = 448.0f / ldexpf(amax, pre);
+    }
     scales[g] = scale;
     for (int32_t i = 0; i < 128; i++) {
-      float v = oracle_bf16_to_f32(xrow[128 * g + i]);
+      float v = ldexpf(oracle_bf16_to_f32(xrow[128 * g + i]), pre);
       float prod = v * inv;
       q[128 * g + i] = oracle_f32_to_e4m3(prod);
     }

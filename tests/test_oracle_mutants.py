@@ -55,6 +55,12 @@ MUTANTS = {
     "ll_slot": ("slot_of[q] = ((e * R) + s) * M + cnt[e];", "slot_of[q] = ((s * E) + e) * M + cnt[e];"),
     # low-latency layout: overflow check off by one
     "ll_overflow": ("if (cnt[e] >= M) {", "if (cnt[e] > M) {"),
+    # quantiser: no rescale where 448/amax overflows (zeros become NaN, small
+    # values saturate to +-amax)
+    "fp8_tiny": ("if (isinf(inv)) {", "if (0) {"),
+    # quantiser: the rescale applied to the inverse but not to the values
+    "fp8_tiny_vals": ("float v = ldexpf(oracle_bf16_to_f32(xrow[128 * g + i]), pre);",
+                      "float v = oracle_bf16_to_f32(xrow[128 * g + i]);"),
     # fp8 dispatch: scales copied to the wrong row
     "fp8_copy": ("memcpy(recv_scales + (int64_t)s * G, sc", "memcpy(recv_scales + (int64_t)t * G, sc"),
     # pre-quantised pass-through: scales taken from the wrong token row
@@ -80,6 +86,7 @@ def _pins(orc):
     yield "e4m3_torch", lambda: tf.test_e4m3_encode_matches_torch_in_range(orc)
     yield "bf16_torch", lambda: tf.test_bf16_round_matches_torch(orc)
     yield "fp8_closed", lambda: tf.test_quantize_amax_maps_to_448_and_error_bound(orc)
+    yield "fp8_pow2", lambda: tf.test_quantize_codes_invariant_under_power_of_two_scaling(orc)
     for w in tdc.CASES:
         yield f"copy_{w.name}", (lambda w=w: tdc.test_dispatch_bf16_is_row_copy(orc, w))
         yield f"rand_{w.name}", (lambda w=w: tdc.test_combine_random_expert_outputs(orc, w))
