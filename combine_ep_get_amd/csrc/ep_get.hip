@@ -105,31 +105,6 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float32 -> OCP E4M3FN code, round to nearest even, saturating at +-448.
-//  |y| >= 448     : largest finite code 0x7E (also +-inf)
-//  |y| >= 2^-6    : normal; keep 3 mantissa bits with RNE on bit 20 of the
-//                   float32 pattern, then rebias the exponent 127 -> 7
-//  |y| <  2^-6    : subnormal; code = rint(|y| * 2^9) in 0..8 (8 is the
-//                   smallest normal, which is then the right answer)
-//  NaN            : 0x7F with the sign
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
-  uint32_t u = __float_as_uint(y);
-  uint32_t s = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a > 0x7F800000u) {
-    code = 0x7Fu;
-  } else if (a >= 0x43E00000u) {
-    code = 0x7Eu;
-  } else if (a >= 0x3C800000u) {
-    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  } else {
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  }
-  return s | code;
-}
-
 // ---------------------------------------------------------------- layout
 // Work split shared by the host (workspace sizing) and the launches: blocks
 // never straddle a source rank, so the per-source sums are sums over whole
@@ -826,12 +801,21 @@ __device__ __forceinline__ void quant_row_fp8(const u32x4* __restrict__ row,
       am = fmaxf(am, __shfl_xor(am, 4));
       const bool zero = (am == 0.0f);
       const float scale = zero ? 1.0f : am / 448.0f;
-      const float inv = 448.0f / am;
+      float inv = 448.0f / am;
       u32x4 q;
-      if (!zero && __builtin_isfinite(inv)) {
+      if (!zero) {
+        if (!__builtin_isfinite(inv)) {
+          // amax < 448/FLT_MAX: the inverse overflows.  The codes approximate
+          // v * 448/amax, which multiplying the whole group by 2^64 (exact for
+          // bf16 values) leaves unchanged, so the scaled group is quantised.
+          inv = 448.0f / (am * 0x1p64f);
+#pragma unroll
+          for (int j = 0; j < 16; j++) f[j] *= 0x1p64f;
+        }
         // |f * inv| <= 448 (1 + 2^-23) < 464 here, where the hardware
-        // conversion (v_cvt_pk_fp8_f32, OCP E4M3 with RNE) equals
-        // e4m3_rne_sat bit for bit (checked on all 2^32 inputs)
+        // conversion (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even,
+        // saturating) is the contract's encoder; a GPU test compares it
+        // with the oracle's encoder on every float32 below 464 in magnitude
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           const float p0 = f[4 * j] * inv, p1 = f[4 * j + 1] * inv;
@@ -841,18 +825,12 @@ __device__ __forceinline__ void quant_row_fp8(const u32x4* __restrict__ row,
           q[j] = (uint32_t)word;
         }
       } else {
-        // all-zero group (signed zero codes), or amax so small that 448/amax
-        // overflows: the software encoder saturates as the contract says
+        // all-zero group: scale 1, each zero keeps its sign
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           uint32_t word = 0;
 #pragma unroll
-          for (int b = 0; b < 4; b++) {
-            const float fv = f[4 * j + b];
-            const uint32_t code = zero ? ((__float_as_uint(fv) >> 24) & 0x80u)
-                                       : e4m3_rne_sat(fv * inv);
-            word |= code << (8 * b);
-          }
+          for (int b = 0; b < 4; b++) word |= ((__float_as_uint(f[4 * j + b]) >> 24) & 0x80u) << (8 * b);
           q[j] = word;
         }
       }

@@ -164,7 +164,10 @@ int ep_get_layout(const ep_problem_t* p, const void* topk_idx,
  *                       ep_recv_capacity(p) (else EP_ERR_CAPACITY)
  * FP8: per token and group, amax = max |x|; scale = amax/448 and
  * inv = 448/amax (fp32 divisions); code = E4M3FN(x * inv), round to nearest
- * even, saturating; amax == 0 gives scale 1 and signed zero codes. */
+ * even, saturating; amax == 0 gives scale 1 and signed zero codes.  Where
+ * 448/amax overflows fp32 (amax below about 1.3e-36) the group's values and
+ * amax are first multiplied by 2^64 (exact), which changes no code of a
+ * group whose inverse is finite either way; the scale is still amax/448. */
 int ep_dispatch(const ep_problem_t* p, const void* x, const float* topk_weights,
                 const int32_t* slot_of, const int32_t* expert_slot_offset,
                 const int32_t* num_recv_per_expert, void* recv_x, float* recv_scales,

@@ -139,17 +139,28 @@ def test_ragged_chunks_and_large_n():
     run_case(idx, H=8, E=256, R=8, A=128)
 
 
+# bf16 group maxima: ordinary scale factors (exactly 1 among them), and the
+# ones where the float32 inverse 448/amax overflows or only just does not --
+# the smallest bf16 subnormal (2^-133), a mid-range subnormal, the smallest
+# normal (2^-126), about 1e-37 and the two bf16 values around 448/FLT_MAX.
+QUANT_MAXIMA_F32 = (448.0, 1.0, 3.0, 0.7109375, 1e-3, 65504.0, 3.0e38, 1e-30)
+QUANT_MAXIMA_BITS = (0x0001, 0x0015, 0x0080, 0x0208, 0x03E0, 0x03E1)
+
+
 def test_fp8_quantiser_exhaustive_on_device():
     """Every finite bf16 value is quantised by the fused dispatch kernel for
-    several group maxima (so several scale factors, including exactly 1) and
-    the codes and scales are compared with the oracle bit for bit."""
+    several group maxima (so several scale factors, including exactly 1 and
+    the tiny maxima whose inverse overflows float32; every group also holds
+    +0 and -0) and the codes and scales are compared with the oracle bit for
+    bit."""
     allv = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     f = oracle.bf16_to_f32(allv)
     finite = allv[np.isfinite(f)]
     rows = []
-    for m in (448.0, 1.0, 3.0, 0.7109375, 1e-3, 65504.0, 3.0e38, 1e-30):
-        mbits = torch.tensor([m], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy() \
-            .view(np.uint16)[0]
+    maxima = [torch.tensor([m], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy()
+              .view(np.uint16)[0] for m in QUANT_MAXIMA_F32] + \
+        [np.uint16(b) for b in QUANT_MAXIMA_BITS]
+    for mbits in maxima:
         mval = oracle.bf16_to_f32(np.array([mbits]))[0]
         vals = finite[np.abs(oracle.bf16_to_f32(finite)) <= mval]
         n = -(-vals.size // 127)
