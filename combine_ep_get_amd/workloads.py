@@ -135,5 +135,22 @@ def make_expert_out(w: Workload, rows: int, seed: int = 0, chunk_rows: int = 409
     return out
 
 
+def make_expert_out_device(w: Workload, rows: int, seed: int = 0, device="cuda"):
+    """Stand-in expert outputs drawn on the GPU: bf16 N(0,1) [rows, H] from
+    torch's seeded generator on ``device`` (a counter-based stream, so the
+    same seed gives the same tensor on the same software stack).  Used where a
+    host draw of hundreds of millions of values would take tens of seconds;
+    callers that check against the oracle copy the tensor to the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed(_input_seed(w, seed) + 700_000)
+    out = torch.empty((rows, w.H), dtype=torch.bfloat16, device=device)
+    step = 8192
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        out[r0:r1] = torch.randn((r1 - r0, w.H), generator=g, device=device,
+                                 dtype=torch.float32).to(torch.bfloat16)
+    return out
+
+
 def with_routing(w: Workload, **kw) -> Workload:
     return replace(w, **kw)

@@ -65,6 +65,14 @@ def load(path):
     L.oracle_dispatch_fp8.argtypes = [_i32, _i32, _i32, _u16p, _i32p, _u8p, _f32p]
     L.oracle_combine.argtypes = [_i32, _i32, _i32, _vp, _i32, _i32p, _f32p,
                                  _vp, _vp, _vp, _i32]
+    L.oracle_dispatch_bf16_mt.restype = ctypes.c_int
+    L.oracle_dispatch_bf16_mt.argtypes = [_i32, _i32, _i32, _u16p, _i32p, _u16p, ctypes.c_int]
+    L.oracle_dispatch_fp8_mt.restype = ctypes.c_int
+    L.oracle_dispatch_fp8_mt.argtypes = [_i32, _i32, _i32, _u16p, _i32p, _u8p, _f32p,
+                                         ctypes.c_int]
+    L.oracle_combine_mt.restype = ctypes.c_int
+    L.oracle_combine_mt.argtypes = [_i32, _i32, _i32, _vp, _i32, _i32p, _f32p, _vp, _vp,
+                                    ctypes.c_int]
     return L
 
 
@@ -182,16 +190,22 @@ def recv_meta(slot_of, topk_weights, cap):
 
 
 # ---------------------------------------------------------------- dispatch
-def dispatch_bf16(x_bits, slot_of, cap, fill=0):
-    """recv_x[cap, H] (uint16 bits); rows no pair maps to keep ``fill``."""
+def dispatch_bf16(x_bits, slot_of, cap, fill=0, threads=1):
+    """recv_x[cap, H] (uint16 bits); rows no pair maps to keep ``fill``.
+    ``threads`` > 1 runs the threaded driver (token ranges in parallel)."""
     x_bits = _c(x_bits, np.uint16)
     slot_of = _c(slot_of, np.int32)
     N, H = x_bits.shape
     K = slot_of.shape[1]
     recv = np.full((cap, H), fill, np.uint16)
     if N and cap:
-        lib().oracle_dispatch_bf16(N, K, H, x_bits.reshape(-1), slot_of.reshape(-1),
-                                   recv.reshape(-1))
+        if threads > 1:
+            if lib().oracle_dispatch_bf16_mt(N, K, H, x_bits.reshape(-1), slot_of.reshape(-1),
+                                             recv.reshape(-1), int(threads)) != 0:
+                raise RuntimeError("oracle_dispatch_bf16_mt: could not start threads")
+        else:
+            lib().oracle_dispatch_bf16(N, K, H, x_bits.reshape(-1), slot_of.reshape(-1),
+                                       recv.reshape(-1))
     return recv
 
 
@@ -206,7 +220,9 @@ def quantize_rows(x_bits):
     return q, sc
 
 
-def dispatch_fp8(x_bits, slot_of, cap):
+def dispatch_fp8(x_bits, slot_of, cap, threads=1):
+    """(codes [cap, H] uint8, scales [cap, H/128] f32); rows no pair maps to
+    stay zero.  ``threads`` > 1 runs the threaded driver."""
     x_bits = _c(x_bits, np.uint16)
     slot_of = _c(slot_of, np.int32)
     N, H = x_bits.shape
@@ -214,8 +230,13 @@ def dispatch_fp8(x_bits, slot_of, cap):
     q = np.zeros((cap, H), np.uint8)
     sc = np.zeros((cap, H // 128), np.float32)
     if N and cap:
-        lib().oracle_dispatch_fp8(N, K, H, x_bits.reshape(-1), slot_of.reshape(-1),
-                                  q.reshape(-1), sc.reshape(-1))
+        if threads > 1:
+            if lib().oracle_dispatch_fp8_mt(N, K, H, x_bits.reshape(-1), slot_of.reshape(-1),
+                                            q.reshape(-1), sc.reshape(-1), int(threads)) != 0:
+                raise RuntimeError("oracle_dispatch_fp8_mt: could not start threads")
+        else:
+            lib().oracle_dispatch_fp8(N, K, H, x_bits.reshape(-1), slot_of.reshape(-1),
+                                      q.reshape(-1), sc.reshape(-1))
     return q, sc
 
 
@@ -252,10 +273,11 @@ def accumulate_stats(count, stats):
 
 
 # ---------------------------------------------------------------- combine
-def combine(expert_out, slot_of, topk_weights, tokens=None):
+def combine(expert_out, slot_of, topk_weights, tokens=None, threads=1):
     """Return (y bf16 bits, acc float32) for all tokens or for ``tokens``.
 
     ``expert_out`` is either uint16 (bf16 bits) or float32, shape [cap, H].
+    ``threads`` > 1 (all tokens only) runs the threaded driver.
     """
     slot_of = _c(slot_of, np.int32)
     w = _c(topk_weights, np.float32)
@@ -273,7 +295,13 @@ def combine(expert_out, slot_of, topk_weights, tokens=None):
     y = np.zeros((rows, H), np.uint16)
     acc = np.zeros((rows, H), np.float32)
     if rows and H:
-        lib().oracle_combine(N, K, H, eo.ctypes.data, is_f32, slot_of.reshape(-1),
-                             w.reshape(-1), y.ctypes.data, acc.ctypes.data,
-                             None if tok_arr is None else tok_arr.ctypes.data, rows)
+        if threads > 1 and tok_arr is None:
+            if lib().oracle_combine_mt(N, K, H, eo.ctypes.data, is_f32, slot_of.reshape(-1),
+                                       w.reshape(-1), y.ctypes.data, acc.ctypes.data,
+                                       int(threads)) != 0:
+                raise RuntimeError("oracle_combine_mt: could not start threads")
+        else:
+            lib().oracle_combine(N, K, H, eo.ctypes.data, is_f32, slot_of.reshape(-1),
+                                 w.reshape(-1), y.ctypes.data, acc.ctypes.data,
+                                 None if tok_arr is None else tok_arr.ctypes.data, rows)
     return y, acc

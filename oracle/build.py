@@ -1,4 +1,5 @@
-"""Compile the C oracle into ``oracle/liboracle.so`` (gcc, no FMA contraction).
+"""Compile the C oracle (and its threaded driver) into ``oracle/liboracle.so``
+(gcc, no FMA contraction).
 
 TEST INFRASTRUCTURE: the oracle is only loaded by the tests, the smoke check and
 the CPU-baseline leg of the benchmark.
@@ -8,7 +9,9 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
+MT_SRC = os.path.join(HERE, "oracle_mt.c")   # threaded driver over the same functions
 LIB = os.path.join(HERE, "liboracle.so")
+LIBS = ["-lm", "-lpthread"]
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
           "-fexcess-precision=standard", "-fPIC", "-shared", "-Wall", "-Wextra"]
@@ -16,7 +19,7 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", *CFLAGS, SRC, MT_SRC, "-o", tmp, *LIBS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -1,5 +1,6 @@
 """Shared helpers for the GPU tests: move seeded inputs to the device, run the
 three entry points through the C ABI, and compare with the oracle."""
+import os
 import sys
 
 import numpy as np
@@ -56,3 +57,13 @@ def check_combine(y_bits, ref_y, ref_acc):
     d = ulp_dist_bf16(y_bits, ref_y)
     assert d.size == 0 or d.max() <= 1
     return int((d != 0).sum())
+
+
+def oracle_threads():
+    """Threads for the oracle's threaded driver: the CPUs this process may use,
+    at most 16 (a GPU machine's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))

@@ -1,7 +1,8 @@
 """GPU parity of the CU-budget launches (ep_problem_t.cu_budget > 0: persistent
 grids, one workgroup per CU).  Every budget must give the bytes of the
-ordinary launch, which the main parity tests hold to the oracle; the small
-case is also compared with the oracle directly.
+ordinary launch, which the main parity tests hold to the oracle; the ragged
+case and the prefill workload (ordinary launch and one budget) are also
+compared with the oracle directly.
 """
 import numpy as np
 import pytest
@@ -11,7 +12,7 @@ import combine_ep_get_amd as ep
 import oracle
 from combine_ep_get_amd import workloads as wl
 
-from .gpu_util import check_combine, dev_bf16, say
+from .gpu_util import check_combine, dev_bf16, host_u16, oracle_threads, say
 
 pytestmark = pytest.mark.gpu
 
@@ -45,38 +46,64 @@ def _run(w, inp, mode, budget, lay, eo):
     return res
 
 
+def _check_oracle(w, inp, mode, res, cap, eo_bits):
+    """One launch's outputs (from _run) against the oracle: payload with zeroed
+    padding rows and the pre-fill elsewhere, scales, tags, running statistics
+    and combine."""
+    r = oracle.layout(inp["topk_idx"], w.E, w.R, w.A)
+    th = oracle_threads()
+    off, cnt = r["expert_slot_offset"], r["num_recv_per_expert"]
+    src, rw = oracle.recv_meta(r["slot_of"], inp["topk_weights"], cap)
+    np.testing.assert_array_equal(res[1].numpy(), src)
+    np.testing.assert_array_equal(res[2].numpy().view(np.uint32), rw.view(np.uint32))
+    want = np.full(w.E, 11, np.int64)
+    oracle.accumulate_stats(cnt, want)
+    np.testing.assert_array_equal(res[3].numpy(), want)
+    if mode == "bf16":
+        rx = oracle.dispatch_bf16(inp["x"], r["slot_of"], cap, fill=0x3C3C, threads=th)
+        oracle.zero_padding(rx, None, off, cnt)
+        np.testing.assert_array_equal(res[0].numpy().view(np.uint16), rx)
+    else:
+        if mode == "fp8":
+            q, sc = oracle.dispatch_fp8(inp["x"], r["slot_of"], cap, threads=th)
+        else:
+            codes, scales = oracle.quantize_rows(inp["x"])
+            q, sc = oracle.dispatch_quantized(codes, scales, r["slot_of"], cap)
+        valid = src >= 0
+        q_want = np.full((cap, w.H), 0x3C, np.uint8)
+        sc_want = np.full((cap, w.H // 128), 7.0, np.float32)
+        q_want[valid] = q[valid]
+        sc_want[valid] = sc[valid]
+        oracle.zero_padding(q_want, sc_want, off, cnt)
+        np.testing.assert_array_equal(res[0].numpy().reshape(cap, w.H), q_want)
+        np.testing.assert_array_equal(res[5].numpy().view(np.uint32), sc_want.view(np.uint32))
+    ref_y, ref_acc = oracle.combine(eo_bits, r["slot_of"], inp["topk_weights"], threads=th)
+    assert check_combine(res[4].numpy().view(np.uint16), ref_y, ref_acc) == 0
+
+
 @pytest.mark.parametrize("mode", ["bf16", "fp8", "prequant"])
 @pytest.mark.parametrize("cid", [0, 3])
 def test_budget_matches_ordinary_launch(cid, mode):
+    """Every budget gives the ordinary launch's bytes; the ordinary launch and
+    one budgeted launch are also held to the oracle directly."""
     w = RAGGED if cid == 0 else wl.CONFIGS[cid]
     inp = wl.make_inputs(w, 0)
     say(f"CU budget parity {w.desc} mode={mode}")
     idx = torch.from_numpy(inp["topk_idx"]).cuda()
     lay = ep.get_layout(idx, w.E, w.R, w.A)
-    eo_bits = wl.make_expert_out(w, lay.capacity, 0)
-    eo = dev_bf16(eo_bits)
+    eo = wl.make_expert_out_device(w, lay.capacity, 0)
+    eo_bits = host_u16(eo)
     ref = _run(w, inp, mode, 0, lay, eo)
     budgets = [1, 3, 256] if cid == 0 else [5, 64, 255, 4096]
+    got = None
     for b in budgets:
         got = _run(w, inp, mode, b, lay, eo)
         for i, (a, c) in enumerate(zip(ref, got)):
             assert torch.equal(a, c), f"budget {b}: output {i} differs from the ordinary launch"
         say(f"  budget {b}: identical")
-    if cid == 0:
-        # the ordinary launch itself against the oracle
-        r = oracle.layout(inp["topk_idx"], w.E, w.R, w.A)
-        ref_y, ref_acc = oracle.combine(eo_bits, r["slot_of"], inp["topk_weights"])
-        assert check_combine(ref[4].numpy().view(np.uint16), ref_y, ref_acc) == 0
-        want = np.full(w.E, 11, np.int64)
-        oracle.accumulate_stats(r["num_recv_per_expert"], want)
-        np.testing.assert_array_equal(ref[3].numpy(), want)
-        src, _ = oracle.recv_meta(r["slot_of"], inp["topk_weights"], lay.capacity)
-        np.testing.assert_array_equal(ref[1].numpy(), src)
-        if mode == "bf16":
-            rx = oracle.dispatch_bf16(inp["x"], r["slot_of"], lay.capacity, fill=0x3C3C)
-            oracle.zero_padding(rx, None, r["expert_slot_offset"], r["num_recv_per_expert"])
-            np.testing.assert_array_equal(ref[0].numpy().view(np.uint16), rx)
-
+    _check_oracle(w, inp, mode, ref, lay.capacity, eo_bits)
+    _check_oracle(w, inp, mode, got, lay.capacity, eo_bits)
+    say(f"  ordinary launch and budget {budgets[-1]} equal the oracle")
 
 
 EDGE = [(wl.custom(N=48, H=136, E=16, K=12, R=4, A=3, name="k12_h136"), "bf16"),

@@ -113,7 +113,8 @@ def test_planted_mistake_is_caught(tmp_path, name):
     cpath = tmp_path / "oracle_mutant.c"
     cpath.write_text(mutated)
     so = tmp_path / "liboracle_mutant.so"
-    subprocess.run(["gcc", *obuild.CFLAGS, str(cpath), "-o", str(so), "-lm"], check=True)
+    subprocess.run(["gcc", *obuild.CFLAGS, str(cpath), obuild.MT_SRC, "-o", str(so), *obuild.LIBS],
+                   check=True)
     caught = []
     with oracle.swapped(str(so)):
         for pin, fn in _pins(oracle):
@@ -129,7 +130,8 @@ def test_planted_mistake_is_caught(tmp_path, name):
 def test_unmutated_copy_passes_all_pins(tmp_path):
     so = tmp_path / "liboracle_copy.so"
     shutil.copy(obuild.SRC, tmp_path / "o.c")
-    subprocess.run(["gcc", *obuild.CFLAGS, str(tmp_path / "o.c"), "-o", str(so), "-lm"], check=True)
+    subprocess.run(["gcc", *obuild.CFLAGS, str(tmp_path / "o.c"), obuild.MT_SRC, "-o", str(so),
+                    *obuild.LIBS], check=True)
     with oracle.swapped(str(so)):
         for _, fn in _pins(oracle):
             fn()
