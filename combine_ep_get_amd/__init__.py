@@ -71,7 +71,9 @@ class LLArgs(ctypes.Structure):
 
 EXPORTS = ("ep_recv_capacity", "ep_workspace_bytes", "ep_get_layout", "ep_dispatch",
            "ep_dispatch_ex", "ep_combine", "ep_layout_error", "ep_status_str", "ep_ll_capacity",
-           "ep_ll_dispatch", "ep_ll_dispatch_ex")
+           "ep_ll_dispatch", "ep_ll_dispatch_ex", "ep_get_layout_noalloc")
+EP_ERR_SCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 2 << 20
 EP_LAYOUT_ERR_OVERFLOW = 2
 
 
@@ -104,6 +106,8 @@ def load(path):
     L.ep_workspace_bytes.argtypes = [P]
     L.ep_get_layout.restype = ctypes.c_int
     L.ep_get_layout.argtypes = [P] + [vp] * 9
+    L.ep_get_layout_noalloc.restype = ctypes.c_int
+    L.ep_get_layout_noalloc.argtypes = [P] + [vp] * 9
     L.ep_dispatch.restype = ctypes.c_int
     L.ep_dispatch.argtypes = [P] + [vp] * 9 + [i64, vp]
     L.ep_dispatch_ex.restype = ctypes.c_int
@@ -237,6 +241,24 @@ def get_layout(topk_idx, num_experts, num_ranks, expert_alignment=1, out=None):
                              _ptr(out.num_recv_per_expert), _ptr(out.expert_slot_offset),
                              _ptr(out.slot_of), _ptr(out.workspace), _stream())
     _check("ep_get_layout", rc)
+    return out
+
+
+def get_layout_noalloc(topk_idx, out, error_word=None):
+    """ep_get_layout_noalloc: the layout of ``topk_idx`` into the preallocated
+    ``out`` (from alloc_layout; its workspace is not used) with the library's
+    static scratch as workspace; ``error_word`` ([1] int32 on the GPU) receives
+    the error bits when given.  Nothing is allocated."""
+    nb = _idx_bytes(topk_idx)
+    _need(topk_idx, topk_idx.dtype, (out.num_tokens, out.num_topk), "topk_idx")
+    p = out.problem()
+    p.topk_idx_bytes = nb
+    rc = lib().ep_get_layout_noalloc(ctypes.byref(p), _ptr(topk_idx),
+                                     _ptr(out.num_tokens_per_rank),
+                                     _ptr(out.num_tokens_per_expert), _ptr(out.is_token_in_rank),
+                                     _ptr(out.num_recv_per_expert), _ptr(out.expert_slot_offset),
+                                     _ptr(out.slot_of), _ptr(error_word), _stream())
+    _check("ep_get_layout_noalloc", rc)
     return out
 
 
@@ -460,6 +482,7 @@ def ll_dispatch(x, topk_idx, topk_weights, num_experts, num_ranks, max_tokens_pe
 ep_recv_capacity = recv_capacity
 ep_workspace_bytes = workspace_bytes
 ep_get_layout = get_layout
+ep_get_layout_noalloc = get_layout_noalloc
 ep_dispatch = dispatch
 ep_dispatch_ex = dispatch
 ep_combine = combine

@@ -1503,14 +1503,15 @@ template <typename I>
 int run_layout(const ep_problem_t* p, const I* topk_idx, int32_t* num_tokens_per_rank,
                int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
                int32_t* num_recv_per_expert, int32_t* expert_slot_offset, int32_t* slot_of,
-               void* workspace, hipStream_t st) {
+               void* workspace, int32_t* err_word, hipStream_t st) {
   int rc;
   const int N = p->num_tokens;
   const Plan pl = make_plan(p);
   const int K = p->num_topk, E = p->num_experts, R = p->num_ranks;
   const int T = N / R, L = E / R;
   char* ws = (char*)workspace;
-  int32_t* err = (int32_t*)(ws + pl.o_err);
+  // the error word: the workspace's own, unless the caller names another
+  int32_t* err = err_word ? err_word : (int32_t*)(ws + pl.o_err);
   int32_t* blk_cnt = (int32_t*)(ws + pl.o_cnt);
   int32_t* blk_rank = (int32_t*)(ws + pl.o_rank);
   int32_t* blk_err = (int32_t*)(ws + pl.o_berr);
@@ -1596,6 +1597,39 @@ void launch_ll(int grid, size_t lds, hipStream_t st, const ep_problem_t* p,
 
 }  // namespace
 
+// ------------------------------------------------------------ static scratch
+// The layout workspace of ep_get_layout_noalloc, for callers that cannot
+// allocate: a file-scope device array, one copy per GPU, held until the
+// process ends.  Host code never uses its name as an address (on the host it
+// is only a stand-in symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address reaches the kernels.  Every call on one GPU shares the
+// array; the layout kernels write every word they later read, so it needs no
+// clearing, and calls that overlap on one GPU race.
+constexpr int64_t kScratchBytes = EP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+int scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return EP_ERR_UNSUPPORTED;
+  void* ptr = cache[dev].load();
+  if (!ptr) {
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      EP_LOG("hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      return EP_ERR_HIP;
+    }
+    cache[dev].store(ptr);
+  }
+  *out = ptr;
+  return EP_OK;
+}
+}  // namespace
+
 // ===================================================================== C ABI
 extern "C" {
 
@@ -1627,10 +1661,38 @@ int ep_get_layout(const ep_problem_t* p, const void* topk_idx, int32_t* num_toke
   if (p->topk_idx_bytes == 8)
     return run_layout(p, (const int64_t*)topk_idx, num_tokens_per_rank, num_tokens_per_expert,
                       is_token_in_rank, num_recv_per_expert, expert_slot_offset, slot_of,
-                      workspace, st);
+                      workspace, nullptr, st);
   return run_layout(p, (const int32_t*)topk_idx, num_tokens_per_rank, num_tokens_per_expert,
                     is_token_in_rank, num_recv_per_expert, expert_slot_offset, slot_of,
-                    workspace, st);
+                    workspace, nullptr, st);
+}
+
+int ep_get_layout_noalloc(const ep_problem_t* p, const void* topk_idx,
+                          int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                          uint8_t* is_token_in_rank, int32_t* num_recv_per_expert,
+                          int32_t* expert_slot_offset, int32_t* slot_of, int32_t* error_word,
+                          void* stream) {
+  int rc = validate_layout(p);
+  if (rc != EP_OK) return rc;
+  const int N = p->num_tokens;
+  if (!num_tokens_per_rank || !num_tokens_per_expert || !num_recv_per_expert ||
+      !expert_slot_offset)
+    return EP_ERR_INVALID_ARG;
+  if (N > 0 && (!topk_idx || !is_token_in_rank || !slot_of)) return EP_ERR_INVALID_ARG;
+  if (make_plan(p).bytes > kScratchBytes) return EP_ERR_SCRATCH;
+  rc = check_device();
+  if (rc != EP_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != EP_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (p->topk_idx_bytes == 8)
+    return run_layout(p, (const int64_t*)topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                      is_token_in_rank, num_recv_per_expert, expert_slot_offset, slot_of, ws,
+                      error_word, st);
+  return run_layout(p, (const int32_t*)topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                    is_token_in_rank, num_recv_per_expert, expert_slot_offset, slot_of, ws,
+                    error_word, st);
 }
 
 int ep_dispatch_ex(const ep_problem_t* p, const ep_dispatch_args_t* a, void* stream) {
@@ -1942,6 +2004,8 @@ const char* ep_status_str(int status) {
     case EP_ERR_CAPACITY: return "receive capacity below N*K + E*(A-1)";
     case EP_ERR_HIP: return "HIP error";
     case EP_ERR_UNSUPPORTED: return "device is not gfx950";
+    case EP_ERR_SCRATCH:
+      return "layout workspace larger than the static scratch of ep_get_layout_noalloc";
     default: return "unknown status";
   }
 }

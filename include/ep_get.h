@@ -39,7 +39,8 @@
  *   - Return values: EP_OK, or an EP_ERR_* code.  Argument checks run on the
  *     host only and never synchronise.  No C++ exception crosses this ABI.
  *   - The library keeps no mutable global state besides per-device caches of
- *     the architecture check and of the LDS size; concurrent calls need
+ *     the architecture check, the LDS size and the scratch address, and the
+ *     static scratch array of ep_get_layout_noalloc; concurrent calls need
  *     distinct workspaces.
  *   - Set EP_GET_LOG=1 in the environment to print launch shapes to stderr.
  */
@@ -58,7 +59,8 @@ enum {
   EP_ERR_INVALID_ARG = 1, /* a size, pointer or divisibility rule is violated      */
   EP_ERR_CAPACITY = 2,    /* recv_capacity below ep_recv_capacity()                */
   EP_ERR_HIP = 3,         /* a HIP launch or copy failed (logged with EP_GET_LOG)  */
-  EP_ERR_UNSUPPORTED = 4  /* the current device is not gfx950                      */
+  EP_ERR_UNSUPPORTED = 4, /* the current device is not gfx950                      */
+  EP_ERR_SCRATCH = 5      /* ep_get_layout_noalloc: workspace above its scratch     */
 };
 
 /* Compile-time limits of the library. */
@@ -141,6 +143,25 @@ int ep_get_layout(const ep_problem_t* p, const void* topk_idx,
                   uint8_t* is_token_in_rank, int32_t* num_recv_per_expert,
                   int32_t* expert_slot_offset, int32_t* slot_of, void* workspace,
                   void* stream);
+
+/* ep_get_layout without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array
+ * of EP_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends (every valid descriptor's ep_workspace_bytes fits in it;
+ * a larger one returns EP_ERR_SCRATCH without launching).  The call itself
+ * allocates nothing.  All other arguments and outputs are those of
+ * ep_get_layout, plus
+ *   error_word  [1] int32 device pointer or NULL: receives the error bits
+ *               (EP_LAYOUT_ERR_INDEX) that ep_layout_error would report.
+ * The array needs no initialisation; every call on one GPU shares it, so
+ * calls that overlap on one GPU (concurrent streams) race. */
+#define EP_NOALLOC_SCRATCH_BYTES (2u << 20)
+int ep_get_layout_noalloc(const ep_problem_t* p, const void* topk_idx,
+                          int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                          uint8_t* is_token_in_rank, int32_t* num_recv_per_expert,
+                          int32_t* expert_slot_offset, int32_t* slot_of, int32_t* error_word,
+                          void* stream);
 
 /* Dispatch: copy (bf16) or quantise-and-copy (e4m3) every token row into the
  * slots slot_of names, and tag every slot with its source and weight.

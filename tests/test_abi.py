@@ -62,9 +62,10 @@ def test_capacity_and_workspace():
 
 def test_status_strings():
     L = ep.lib()
-    for code in range(5):
+    for code in range(6):
         assert L.ep_status_str(code)
     assert b"unknown" in L.ep_status_str(99)
+    assert b"scratch" in L.ep_status_str(ep.EP_ERR_SCRATCH)
 
 
 def _p(**kw):
@@ -86,6 +87,32 @@ def test_layout_rejects_bad_descriptors(kw):
     fake = ctypes.c_void_p(256)   # never dereferenced: validation runs first
     rc = L.ep_get_layout(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, None)
     assert rc == 1
+
+
+@pytest.mark.parametrize("kw", BAD, ids=[str(b) for b in BAD])
+def test_noalloc_layout_rejects_bad_descriptors(kw):
+    L = ep.lib()
+    p = _p(**kw)
+    fake = ctypes.c_void_p(256)   # never dereferenced: validation runs first
+    rc = L.ep_get_layout_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
+                                 None)
+    assert rc == 1
+
+
+def test_noalloc_layout_missing_outputs_and_scratch_bound():
+    L = ep.lib()
+    fake = ctypes.c_void_p(256)
+    p = _p()
+    # outputs that must exist
+    assert L.ep_get_layout_noalloc(ctypes.byref(p), fake, None, fake, fake, fake, fake, fake,
+                                   None, None) == 1
+    assert L.ep_get_layout_noalloc(ctypes.byref(p), None, fake, fake, fake, fake, fake, fake,
+                                   None, None) == 1
+    # the static scratch covers the largest workspace any valid descriptor needs
+    worst = max(ep.workspace_bytes(n, k, 1024, r, 1)
+                for r in (1, 8, 64, 256) for k in (1, 8, 32)
+                for n in (r, 64 * r, 1024 * r, 65536 * r // 8) if n * k < 2 ** 31 - 1)
+    assert 0 < worst <= ep.NOALLOC_SCRATCH_BYTES
 
 
 def test_payload_rejects_bad_descriptors():
