@@ -16,8 +16,11 @@ tokens/s.  Algorithmic bytes: dispatch 2NH + 2NKH (bf16) or 2NH + NKH +
 4NK(H/128) (e4m3), combine 2NKH + 2NH.  Layout time counts inside the step.
 
 Prints ONE JSON line.  Extra keys beside the required ones: tokens_per_s,
-hbm_frac, per-kernel times, the measured copy/write ceilings, the roofline of
-the dominant kernel and the CPU oracle baseline.
+hbm_frac, per-kernel times, the roofline of the dominant kernel, the HBM
+ceilings measured on the same box (linear copy / write / read, and dispatch's
+and combine's own access patterns on the workload's slot map) with each
+kernel's fraction of its pattern's ceiling, cold-cache step times, and the CPU
+oracle baseline (threaded and single-threaded).
 """
 import argparse
 import ctypes
@@ -73,66 +76,141 @@ def read_traffic(kernel, workload):
         return None
 
 
+def _cpu_info():
+    """Model name and a few identifying fields of the host CPU (/proc/cpuinfo)."""
+    info = {}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if ":" not in line:
+                if info:
+                    break
+                continue
+            k, v = (t.strip() for t in line.split(":", 1))
+            if k in ("model name", "cpu family", "model", "stepping", "cpu MHz") and k not in info:
+                info[k] = v
+    except OSError:
+        pass
+    return info
+
+
+def oracle_threads():
+    """CPUs this process may use, at most 16 (a GPU machine's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(w, inp, eo_bits, budget_s):
-    """The oracle as it stands, single-threaded, on the same prefill batch."""
+    """The oracle as it stands on the same batch, timed on this host: single
+    threaded, and through its threaded driver (layout and slot tags serial,
+    dispatch and combine over token ranges on every usable CPU, at most 16).
+    Each form runs full steps for about half of ``budget_s``; the outputs of
+    the two forms' last steps are compared byte for byte."""
     import oracle
     cap = oracle.capacity(w.N, w.K, w.E, w.A)
     disp_b, comb_b = algorithmic_bytes(w)
-    reps, t_total = 0, 0.0
-    while t_total < budget_s or reps == 0:
-        t0 = time.perf_counter()
+
+    def step(th):
         lay = oracle.layout(inp["topk_idx"], w.E, w.R, w.A)
         if w.fp8:
-            oracle.dispatch_fp8(inp["x"], lay["slot_of"], cap)
+            d = oracle.dispatch_fp8(inp["x"], lay["slot_of"], cap, threads=th)
         else:
-            oracle.dispatch_bf16(inp["x"], lay["slot_of"], cap)
-        oracle.recv_meta(lay["slot_of"], inp["topk_weights"], cap)
-        oracle.combine(eo_bits, lay["slot_of"], inp["topk_weights"])
-        t_total += time.perf_counter() - t0
-        reps += 1
-    step_s = t_total / reps
-    model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return {"value": round((disp_b + comb_b) / step_s / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
-            "sample": f"{reps} full steps (layout+dispatch+combine) of the {w.name} batch, "
-                      f"{w.N} tokens, single thread, {step_s * 1e3:.1f} ms/step",
-            "tokens_per_s": round(w.N / step_s, 1)}
+            d = (oracle.dispatch_bf16(inp["x"], lay["slot_of"], cap, threads=th),)
+        meta = oracle.recv_meta(lay["slot_of"], inp["topk_weights"], cap)
+        y = oracle.combine(eo_bits, lay["slot_of"], inp["topk_weights"], threads=th)
+        return [lay["slot_of"], *d, *meta, *y]
+
+    def timed(th):
+        reps, t_total, out = 0, 0.0, None
+        while t_total < budget_s / 2 or reps == 0:
+            out = None
+            t0 = time.perf_counter()
+            out = step(th)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        return t_total / reps, reps, out
+
+    nth = oracle_threads()
+    s1, r1, o1 = timed(1)
+    sn, rn, on = timed(nth)
+    identical = all(np.array_equal(a.view(np.uint8), b.view(np.uint8)) for a, b in zip(o1, on))
+    del o1, on
+
+    def row(step_s, reps, th):
+        return {"value": round((disp_b + comb_b) / step_s / 1e9, 3), "unit": "GB/s",
+                "cores": th, "tokens_per_s": round(w.N / step_s, 1),
+                "ms_per_step": round(step_s * 1e3, 1), "steps": reps}
+
+    res = {"kind": "oracle", **row(sn, rn, nth),
+           "sample": f"full steps (layout + dispatch + slot tags + combine) of the {w.name} batch, "
+                     f"{w.N} tokens: {rn} with the threaded driver ({nth} threads: layout and "
+                     f"tags serial, dispatch and combine over token ranges), {r1} single-"
+                     f"threaded; same algorithmic bytes as the GPU figure",
+           "single_thread": row(s1, r1, 1),
+           "threaded_identical_to_single": bool(identical),
+           "cpu": _cpu_info(), "host_cpus": os.cpu_count()}
+    return res
 
 
-def ceilings(nbytes=1 << 30):
-    """Measured HBM copy, pure-write and pure-read bandwidth (GB/s) on this GPU."""
+def ceilings(per_launch_ms, w, slot_of, x, recv_x, eo, nbytes=1 << 30):
+    """What this GPU's HBM delivers, timed like the EP kernels (a graph of
+    back-to-back launches): linear copy / write / read over 1 GiB with four or
+    one 16-byte accesses per thread, and the two traffic patterns of the path
+    on the workload's own slot map -- dispatch's (each token row read once and
+    written to its K slots) and combine's (K slot rows gathered, one row
+    written) -- with no arithmetic.  GB/s of the patterns use the same
+    algorithmic bytes as the kernels they bound."""
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "combine_ep_get_amd", "_lib", "libepceil.so"))
-    lib.epc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    lib.epc_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
-    lib.epc_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.epc_copy_p.argtypes = [vp, vp, i64, ctypes.c_int, vp]
+    lib.epc_write_p.argtypes = [vp, i64, ctypes.c_uint32, ctypes.c_int, vp]
+    lib.epc_read_p.argtypes = [vp, i64, ctypes.c_int, vp, vp]
+    lib.epc_scatter.argtypes = [vp, vp, vp, i32, i32, i64, vp]
+    lib.epc_gather.argtypes = [vp, vp, vp, i32, i32, i64, vp]
+
+    def cur():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
     a = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.empty(256, dtype=torch.int32, device="cuda")
-    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     res = {}
     for name, fn, moved in (
-            ("copy", lambda: lib.epc_copy(b.data_ptr(), a.data_ptr(), nbytes, st), 2),
-            ("write", lambda: lib.epc_write(a.data_ptr(), nbytes, 7, st), 1),
-            ("read", lambda: lib.epc_read(a.data_ptr(), nbytes, sink.data_ptr(), st), 1)):
-        for _ in range(3):
-            assert fn() == 0
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name + "_gbs"] = round(moved * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+            ("copy", lambda: lib.epc_copy_p(b.data_ptr(), a.data_ptr(), nbytes, 4, cur()), 2),
+            ("copy1", lambda: lib.epc_copy_p(b.data_ptr(), a.data_ptr(), nbytes, 1, cur()), 2),
+            ("write", lambda: lib.epc_write_p(a.data_ptr(), nbytes, 7, 4, cur()), 1),
+            ("write1", lambda: lib.epc_write_p(a.data_ptr(), nbytes, 7, 1, cur()), 1),
+            ("read", lambda: lib.epc_read_p(a.data_ptr(), nbytes, 4, sink.data_ptr(), cur()), 1),
+            ("read1", lambda: lib.epc_read_p(a.data_ptr(), nbytes, 1, sink.data_ptr(), cur()), 1)):
+        assert fn() == 0
+        res[name + "_gbs"] = round(moved * nbytes / (per_launch_ms(fn) * 1e-3) / 1e9, 1)
     del a, b
+    disp_b, comb_b = algorithmic_bytes(w)
+    row_b = 2 * w.H
+    if not w.fp8 and row_b <= 16384:
+        fn = lambda: lib.epc_scatter(x.data_ptr(), recv_x.data_ptr(), slot_of.data_ptr(),  # noqa: E731
+                                     w.N, w.K, row_b, cur())
+        assert fn() == 0
+        res["scatter_gbs"] = round(disp_b / (per_launch_ms(fn) * 1e-3) / 1e9, 1)
+    if w.K <= 8 and row_b <= 16384:
+        yt = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: lib.epc_gather(eo.data_ptr(), yt.data_ptr(), slot_of.data_ptr(),  # noqa: E731
+                                    w.N, w.K, row_b, cur())
+        assert fn() == 0
+        res["gather_gbs"] = round(comb_b / (per_launch_ms(fn) * 1e-3) / 1e9, 1)
     return res
+
+
+def lds_info():
+    """LDS per workgroup (what a CU-budget workgroup reserves) and per CU."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_ep_get_amd", "_lib", "libepceil.so"))
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    if lib.epc_lds_info(ctypes.byref(a), ctypes.byref(b)) != 0:
+        return None
+    return {"lds_per_workgroup": a.value, "lds_per_cu": b.value}
 
 
 def _csv_rows(path):
@@ -151,12 +229,15 @@ def summarize(args):
     w = wl.CONFIGS[args.config]
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
-    cmd_base = f"python3 bench.py --config {args.config}"
+    # the profiles are taken from /tmp (rocprofv3 writes its scratch there), so
+    # bench.py is named by its path; <repo> stands for the repository root
+    cmd_base = f"python3 <repo>/bench.py --config {args.config}"
     # kernel trace statistics
     stats = _csv_rows(os.path.join(args.trace_dir, "run_kernel_stats.csv"))
     lines = [f"# rocprofv3 kernel statistics: {w.desc}",
              f"# command: cd /tmp && rocprofv3 --kernel-trace --stats -T -f csv -d <out> -o run -- "
              f"{cmd_base} --steps 20 --warmup 5 --cpu-seconds 0 --no-ceiling --cold-steps 0",
+             "# <repo> is the repository root; the command runs from /tmp",
              f"# kernel source sha256 (comments and blank space stripped): {source_sha()}",
              f"{'kernel':28s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
     for r in stats:
@@ -194,6 +275,7 @@ def summarize(args):
                f"{cmd_base} --steps 3 --warmup 1 --cpu-seconds 0 --cold-steps 0",
                f"#           cd /tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv -d <out> -o run -- "
                f"{cmd_base} --steps 3 --warmup 1 --cpu-seconds 0 --cold-steps 0",
+               "# <repo> is the repository root; the commands run from /tmp",
                "# scale: counter KiB of the 1 GiB copy kernel in the same run -> bytes",
                "# source_sha256: ep_get.hip with comments and blank space stripped",
                f"kernel: {kname}",
@@ -509,12 +591,30 @@ def main():
                         "compute_units": props.multi_processor_count,
                         "memory_gib": round(props.total_memory / 2 ** 30, 1),
                         "hip": torch.version.hip, "torch": torch.__version__}
+    lds = lds_info()
+    if lds:
+        result["device"].update(lds)
+        if args.cu_budget:
+            # each CU-budget workgroup reserves lds_per_workgroup bytes; more
+            # than half of a CU's LDS means at most one of them per CU
+            result["config"]["cu_budget_lds_per_workgroup"] = lds["lds_per_workgroup"]
+            result["config"]["cu_budget_one_workgroup_per_cu"] = \
+                2 * lds["lds_per_workgroup"] > lds["lds_per_cu"]
     if overlap:
         result["overlap"] = overlap
     if not args.no_ceiling:
-        c = ceilings()
+        print("[bench] HBM ceilings", file=sys.stderr, flush=True)
+        recv_x_t = ll_out[1][0] if args.ll else recv[0]
+        c = ceilings(per_launch_ms, w, lay.slot_of, x, recv_x_t, eo)
         result["ceiling"] = c
-        result["frac_of_copy_ceiling"] = round(gbs / c["copy_gbs"], 4)
+        best_copy = max(c["copy_gbs"], c["copy1_gbs"])
+        result["frac_of_copy_ceiling"] = round(gbs / best_copy, 4)
+        frac = {}
+        if "scatter_gbs" in c:
+            frac["dispatch"] = round(result["kernel_gbs"]["dispatch"] / c["scatter_gbs"], 4)
+        if "gather_gbs" in c:
+            frac["combine"] = round(result["kernel_gbs"]["combine"] / c["gather_gbs"], 4)
+        result["frac_of_pattern_ceiling"] = frac
     if args.cpu_seconds > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, inp, eo_bits, args.cpu_seconds)

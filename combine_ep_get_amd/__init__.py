@@ -476,17 +476,32 @@ def ll_dispatch(x, topk_idx, topk_weights, num_experts, num_ranks, max_tokens_pe
     return lay, (recv_x, scales if use_fp8 else None, src, rw)
 
 
-# The C entry points' own names, for callers who read include/ep_get.h: each
-# is the function above that marshals that entry point's arguments (the
-# *_ex variants are reached through dispatch's / ll_dispatch's options).
+def ep_dispatch_ex(p, args, stream=None):
+    """The C call itself: ``p`` a Problem, ``args`` a DispatchArgs whose fields
+    are device addresses (ints) and sizes, exactly as include/ep_get.h states;
+    enqueued on ``stream`` (a raw hipStream_t as int, default: torch's current
+    stream).  Raises EPError on a non-OK status."""
+    st = _stream() if stream is None else ctypes.c_void_p(stream)
+    _check("ep_dispatch_ex", lib().ep_dispatch_ex(ctypes.byref(p), ctypes.byref(args), st))
+
+
+def ep_ll_dispatch_ex(p, max_tokens_per_rank, args, stream=None):
+    """The C call itself: ``p`` a Problem, ``args`` an LLArgs of device
+    addresses, as include/ep_get.h states; see ep_dispatch_ex."""
+    st = _stream() if stream is None else ctypes.c_void_p(stream)
+    _check("ep_ll_dispatch_ex", lib().ep_ll_dispatch_ex(ctypes.byref(p), int(max_tokens_per_rank),
+                                                        ctypes.byref(args), st))
+
+
+# The other C entry points under their own names, for callers who read
+# include/ep_get.h: each is the function above that marshals that entry
+# point's arguments from tensors.
 ep_recv_capacity = recv_capacity
 ep_workspace_bytes = workspace_bytes
 ep_get_layout = get_layout
 ep_get_layout_noalloc = get_layout_noalloc
 ep_dispatch = dispatch
-ep_dispatch_ex = dispatch
 ep_combine = combine
 ep_layout_error = layout_error
 ep_ll_capacity = ll_capacity
 ep_ll_dispatch = ll_dispatch
-ep_ll_dispatch_ex = ll_dispatch

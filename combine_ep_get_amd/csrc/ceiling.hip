@@ -1,6 +1,23 @@
-// ceiling.hip -- plain streaming kernels used only to measure what this GPU's
-// HBM delivers (copy and pure write), and as the known-size reference when
-// scaling rocprof FETCH_SIZE / WRITE_SIZE counters.  Not part of the EP path.
+// ceiling.hip -- plain kernels that measure what this GPU's HBM delivers for
+// the traffic patterns of the EP path, and the known-size reference used to
+// scale rocprof FETCH_SIZE / WRITE_SIZE counters.  Not part of the EP path:
+// the benchmark times them beside the EP kernels so that each kernel can be
+// judged against the best rate its own access pattern reaches on the same
+// box, as well as against the 8 TB/s peak.
+//
+//   copy / write / read : linear sweeps with P 16-byte accesses per thread
+//                         (P = 4 or 1: fewer accesses per thread, more
+//                         threads, is faster for writes on MI355X);
+//   scatter             : dispatch's traffic without its arithmetic or tags:
+//                         token row t (R 16-byte chunks) is read once and
+//                         written to the K rows map[t][0..K-1] of dst;
+//   gather              : combine's traffic without its arithmetic: the K
+//                         rows map[t][0..K-1] of src are read and one row
+//                         (their XOR, so that no load is dead) is written
+//                         to dst[t].
+// The map is the real slot map of a workload (slot_of), so the addresses are
+// exactly the EP kernels'.  Rows named -1 are skipped (scatter) or read as
+// row 0 (gather, like combine's branch-free loads).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -8,40 +25,43 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kPer = 4;   // 16-byte chunks per thread
 
+template <int P>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict__ src,
                                                         u32x4* __restrict__ dst, int64_t n16) {
-  const int64_t base = ((int64_t)blockIdx.x * kThreads * kPer) + threadIdx.x;
-  u32x4 v[kPer];
+  const int64_t base = ((int64_t)blockIdx.x * kThreads * P) + threadIdx.x;
+  u32x4 v[P];
 #pragma unroll
-  for (int i = 0; i < kPer; i++) {
+  for (int i = 0; i < P; i++) {
     const int64_t j = base + (int64_t)i * kThreads;
     if (j < n16) v[i] = __builtin_nontemporal_load(src + j);
   }
 #pragma unroll
-  for (int i = 0; i < kPer; i++) {
+  for (int i = 0; i < P; i++) {
     const int64_t j = base + (int64_t)i * kThreads;
     if (j < n16) __builtin_nontemporal_store(v[i], dst + j);
   }
 }
 
+template <int P>
 __global__ __launch_bounds__(kThreads) void write_kernel(u32x4* __restrict__ dst, int64_t n16,
                                                          uint32_t value) {
-  const int64_t base = ((int64_t)blockIdx.x * kThreads * kPer) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x * kThreads * P) + threadIdx.x;
   const u32x4 v = {value, value, value, value};
 #pragma unroll
-  for (int i = 0; i < kPer; i++) {
+  for (int i = 0; i < P; i++) {
     const int64_t j = base + (int64_t)i * kThreads;
     if (j < n16) __builtin_nontemporal_store(v, dst + j);
   }
 }
+
+template <int P>
 __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ src,
                                                         int64_t n16, uint32_t* __restrict__ sink) {
-  const int64_t base = ((int64_t)blockIdx.x * kThreads * kPer) + threadIdx.x;
+  const int64_t base = ((int64_t)blockIdx.x * kThreads * P) + threadIdx.x;
   uint32_t x = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; i++) {
+  for (int i = 0; i < P; i++) {
     const int64_t j = base + (int64_t)i * kThreads;
     if (j < n16) {
       const u32x4 v = __builtin_nontemporal_load(src + j);
@@ -50,38 +70,182 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
   }
   if (x == 0x9E3779B9u) sink[threadIdx.x] = x;   // keeps the loads; practically never stores
 }
+
+// Scatter: one wavefront per token; the row is read into registers once
+// (NV chunks per lane) and stored to each of the K rows.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const u32x4* __restrict__ src,
+                                                           u32x4* __restrict__ dst,
+                                                           const int32_t* __restrict__ map,
+                                                           int N, int K, int R) {
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= N) return;
+  const int lane = threadIdx.x & 63;
+  const u32x4* row = src + (int64_t)t * R;
+  u32x4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int c = i * 64 + lane;
+    if (c < R) v[i] = row[c];
+  }
+  for (int k = 0; k < K; k++) {
+    const int s = map[(int64_t)t * K + k];
+    if (s < 0) continue;
+    u32x4* d = dst + (int64_t)s * R;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int c = i * 64 + lane;
+      if (c < R) __builtin_nontemporal_store(v[i], d + c);
+    }
+  }
+}
+
+// Gather: one workgroup of R threads (R <= 1024) per token, one chunk column
+// per thread; all K rows of the token are requested before any is used (K is
+// a template parameter so that the loads are unconditional and in flight
+// together).
+template <int K>
+__global__ __launch_bounds__(1024) void gather_kernel(const u32x4* __restrict__ src,
+                                                      u32x4* __restrict__ dst,
+                                                      const int32_t* __restrict__ map, int N,
+                                                      int R) {
+  const int t = blockIdx.x;
+  const int c = threadIdx.x;
+  if (t >= N || c >= R) return;
+  u32x4 v[K];
+#pragma unroll
+  for (int k = 0; k < K; k++) {
+    int s = map[(int64_t)t * K + k];
+    s = s < 0 ? 0 : s;
+    v[k] = __builtin_nontemporal_load(src + (int64_t)s * R + c);
+  }
+  u32x4 x = v[0];
+#pragma unroll
+  for (int k = 1; k < K; k++) x ^= v[k];
+  __builtin_nontemporal_store(x, dst + (int64_t)t * R + c);
+}
+
+int64_t blocks_of(int64_t n16, int per) { return (n16 + (int64_t)kThreads * per - 1) / ((int64_t)kThreads * per); }
+
+int launched() { return hipGetLastError() == hipSuccess ? 0 : 3; }
 }  // namespace
 
 extern "C" {
-// Read `bytes` (multiple of 16, 16-byte aligned); `sink` must hold 256 uint32.
+// Read `bytes` (multiple of 16, 16-byte aligned) with `per` (1 or 4) 16-byte
+// loads per thread; `sink` must hold 256 uint32.
+int epc_read_p(const void* src, int64_t bytes, int per, void* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 || (uintptr_t)src % 16 || (per != 1 && per != 4)) return 1;
+  const int64_t n16 = bytes / 16, blocks = blocks_of(n16, per);
+  if (blocks == 0) return 0;
+  if (per == 1)
+    read_kernel<1><<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src, n16,
+                                                                           (uint32_t*)sink);
+  else
+    read_kernel<4><<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src, n16,
+                                                                           (uint32_t*)sink);
+  return launched();
+}
+
+// Fill `bytes` (multiple of 16, 16-byte aligned) with a 32-bit pattern,
+// `per` (1 or 4) 16-byte stores per thread.
+int epc_write_p(void* dst, int64_t bytes, uint32_t value, int per, void* stream) {
+  if (bytes < 0 || bytes % 16 || (uintptr_t)dst % 16 || (per != 1 && per != 4)) return 1;
+  const int64_t n16 = bytes / 16, blocks = blocks_of(n16, per);
+  if (blocks == 0) return 0;
+  if (per == 1)
+    write_kernel<1><<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((u32x4*)dst, n16, value);
+  else
+    write_kernel<4><<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((u32x4*)dst, n16, value);
+  return launched();
+}
+
+// Copy `bytes` (multiple of 16, 16-byte aligned pointers) from src to dst,
+// `per` (1 or 4) 16-byte loads and stores per thread.
+int epc_copy_p(void* dst, const void* src, int64_t bytes, int per, void* stream) {
+  if (bytes < 0 || bytes % 16 || ((uintptr_t)dst | (uintptr_t)src) % 16 || (per != 1 && per != 4))
+    return 1;
+  const int64_t n16 = bytes / 16, blocks = blocks_of(n16, per);
+  if (blocks == 0) return 0;
+  if (per == 1)
+    copy_kernel<1><<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src,
+                                                                           (u32x4*)dst, n16);
+  else
+    copy_kernel<4><<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src,
+                                                                           (u32x4*)dst, n16);
+  return launched();
+}
+
+// LDS of the current device: the per-workgroup maximum (what each CU-budget
+// workgroup of the EP library reserves: it asks for sharedMemPerBlock) and
+// the per-CU total.  Returns 0, or 3 when the properties cannot be read.
+int epc_lds_info(int64_t* per_workgroup, int64_t* per_cu) {
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (!per_workgroup || !per_cu) return 1;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return 3;
+  *per_workgroup = (int64_t)prop.sharedMemPerBlock;
+  *per_cu = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
+  return 0;
+}
+
+// The four-access-per-thread forms (the counter-scaling reference).
 int epc_read(const void* src, int64_t bytes, void* sink, void* stream) {
-  if (bytes < 0 || bytes % 16 || (uintptr_t)src % 16) return 1;
-  const int64_t n16 = bytes / 16;
-  const int64_t blocks = (n16 + kThreads * kPer - 1) / (kThreads * kPer);
-  if (blocks == 0) return 0;
-  read_kernel<<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src, n16,
-                                                                      (uint32_t*)sink);
-  return hipGetLastError() == hipSuccess ? 0 : 3;
+  return epc_read_p(src, bytes, 4, sink, stream);
 }
-
-// Copy `bytes` (multiple of 16, 16-byte aligned pointers) from src to dst.
 int epc_copy(void* dst, const void* src, int64_t bytes, void* stream) {
-  if (bytes < 0 || bytes % 16 || ((uintptr_t)dst | (uintptr_t)src) % 16) return 1;
-  const int64_t n16 = bytes / 16;
-  const int64_t blocks = (n16 + kThreads * kPer - 1) / (kThreads * kPer);
-  if (blocks == 0) return 0;
-  copy_kernel<<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src,
-                                                                      (u32x4*)dst, n16);
-  return hipGetLastError() == hipSuccess ? 0 : 3;
+  return epc_copy_p(dst, src, bytes, 4, stream);
+}
+int epc_write(void* dst, int64_t bytes, uint32_t value, void* stream) {
+  return epc_write_p(dst, bytes, value, 4, stream);
 }
 
-// Fill `bytes` (multiple of 16, 16-byte aligned) with a 32-bit pattern.
-int epc_write(void* dst, int64_t bytes, uint32_t value, void* stream) {
-  if (bytes < 0 || bytes % 16 || (uintptr_t)dst % 16) return 1;
-  const int64_t n16 = bytes / 16;
-  const int64_t blocks = (n16 + kThreads * kPer - 1) / (kThreads * kPer);
-  if (blocks == 0) return 0;
-  write_kernel<<<(unsigned)blocks, kThreads, 0, (hipStream_t)stream>>>((u32x4*)dst, n16, value);
-  return hipGetLastError() == hipSuccess ? 0 : 3;
+// Dispatch's pattern: src [N][row_bytes], dst [rows][row_bytes], map [N][K]
+// int32 row indices in [-1, rows).  row_bytes a multiple of 16, at most
+// 16 KiB (1024 chunks); pointers 16-byte aligned.  The caller guarantees the
+// map's range.
+int epc_scatter(const void* src, void* dst, const int32_t* map, int32_t N, int32_t K,
+                int64_t row_bytes, void* stream) {
+  if (N < 0 || K < 1 || row_bytes <= 0 || row_bytes % 16 || row_bytes > 16384 ||
+      ((uintptr_t)src | (uintptr_t)dst) % 16)
+    return 1;
+  if (N == 0) return 0;
+  const int R = (int)(row_bytes / 16);
+  const int blocks = (N + kThreads / 64 - 1) / (kThreads / 64);
+  hipStream_t st = (hipStream_t)stream;
+  const u32x4* s = (const u32x4*)src;
+  u32x4* d = (u32x4*)dst;
+  if (R <= 64 * 4) scatter_kernel<4><<<blocks, kThreads, 0, st>>>(s, d, map, N, K, R);
+  else if (R <= 64 * 8) scatter_kernel<8><<<blocks, kThreads, 0, st>>>(s, d, map, N, K, R);
+  else if (R <= 64 * 14) scatter_kernel<14><<<blocks, kThreads, 0, st>>>(s, d, map, N, K, R);
+  else scatter_kernel<16><<<blocks, kThreads, 0, st>>>(s, d, map, N, K, R);
+  return launched();
+}
+
+// Combine's pattern: src [rows][row_bytes] (rows >= 1), map [N][K] in
+// [-1, rows), dst [N][row_bytes].  K <= 8, row_bytes a multiple of 16, at
+// most 16 KiB.
+int epc_gather(const void* src, void* dst, const int32_t* map, int32_t N, int32_t K,
+               int64_t row_bytes, void* stream) {
+  if (N < 0 || K < 1 || K > 8 || row_bytes <= 0 || row_bytes % 16 || row_bytes > 16384 ||
+      ((uintptr_t)src | (uintptr_t)dst) % 16)
+    return 1;
+  if (N == 0) return 0;
+  const int R = (int)(row_bytes / 16);
+  const int threads = (R + 63) / 64 * 64;
+  hipStream_t st = (hipStream_t)stream;
+  const u32x4* s = (const u32x4*)src;
+  u32x4* d = (u32x4*)dst;
+  switch (K) {
+    case 1: gather_kernel<1><<<N, threads, 0, st>>>(s, d, map, N, R); break;
+    case 2: gather_kernel<2><<<N, threads, 0, st>>>(s, d, map, N, R); break;
+    case 3: gather_kernel<3><<<N, threads, 0, st>>>(s, d, map, N, R); break;
+    case 4: gather_kernel<4><<<N, threads, 0, st>>>(s, d, map, N, R); break;
+    case 5: gather_kernel<5><<<N, threads, 0, st>>>(s, d, map, N, R); break;
+    case 6: gather_kernel<6><<<N, threads, 0, st>>>(s, d, map, N, R); break;
+    case 7: gather_kernel<7><<<N, threads, 0, st>>>(s, d, map, N, R); break;
+    default: gather_kernel<8><<<N, threads, 0, st>>>(s, d, map, N, R); break;
+  }
+  return launched();
 }
 }

@@ -60,18 +60,13 @@
 #ifndef EP_NT_STORE
 #define EP_NT_STORE 1
 #endif
-#ifndef EP_DISPATCH_TPT
-#define EP_DISPATCH_TPT 64
-#endif
 
 namespace {
 
 #ifndef EP_BLOCK
 #define EP_BLOCK 256
 #endif
-constexpr int kThreads = EP_BLOCK;        // threads per block of the row kernels
-constexpr int kWaves = kThreads / 64;
-constexpr int kFillPerThread = 8;         // padding-fill: slots per thread
+constexpr int kThreads = EP_BLOCK;        // threads per block of the small utility kernels
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -585,61 +580,25 @@ __global__ __launch_bounds__(kThreads) void layout_empty_kernel(
 }
 
 // ---------------------------------------------------------------- dispatch
-// Padding / unused slots of [0, cap): source -1, weight 0.  A slot s below
-// off[E] belongs to the expert e with off[e] <= s < off[e+1] (binary search
-// over the offsets staged in LDS) and is padding iff s - off[e] >= count[e].
-template <int BLK>
-__device__ __forceinline__ void stage_offsets(const int32_t* __restrict__ off,
-                                              const int32_t* __restrict__ recv_cnt, int E,
-                                              int* s_off, int* s_cnt) {
-  for (int e = threadIdx.x; e <= E; e += BLK) {
-    s_off[e] = off[e];
-    if (e < E) s_cnt[e] = recv_cnt[e];
-  }
-}
+// Work of a dispatch launch besides the token rows, taken as wavefront items
+// by blocks placed after the payload blocks of the grid (or by the items of a
+// persistent grid), so that it runs alongside them and costs the payload
+// blocks nothing:
+//   - padding tags: every slot of [0, cap) that holds no pair gets source -1
+//     and weight 0.  Item e < E tags expert e's padding slots
+//     [off[e] + cnt[e], off[e+1]) (fewer than A); item E + u tags the slots of
+//     [u * kTailSlots, (u+1) * kTailSlots) at or beyond off[E] (unit u exits at
+//     once when its range lies below off[E]).  No search and no LDS.
+//   - zeroed padding rows (DeepEP's do_zero_padding): item v takes padding
+//     row j = v % (A-1) of expert e = v / (A-1), which exists iff
+//     j < off[e+1] - off[e] - cnt[e]; consecutive items take consecutive rows
+//     of one expert, so items past an expert's padding exit at once.
+//   - the running per-expert receive counts (DeepEP's
+//     cumulative_local_expert_recv_stats): one item.
+// Every range is clamped to [0, cap), so offsets that ep_get_layout did not
+// produce cannot send a store out of the buffers.
+constexpr int kTailSlots = 512;
 
-// Tag slots s0 + j*span + tid, j < kFillPerThread (offsets staged in LDS).
-__device__ __forceinline__ void tag_padding(int64_t s0, int span, int tid, int E, int64_t cap,
-                                            int32_t* __restrict__ recv_src,
-                                            float* __restrict__ recv_w, const int* s_off,
-                                            const int* s_cnt) {
-  const int used = s_off[E];
-#pragma unroll
-  for (int j = 0; j < kFillPerThread; j++) {
-    const int64_t s = s0 + (int64_t)j * span + tid;
-    if (s >= cap) break;
-    bool pad = true;
-    if (s < used) {
-      int lo = 0, hi = E;  // off[lo] <= s < off[hi]
-      while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (s_off[mid] <= s) lo = mid; else hi = mid;
-      }
-      pad = (s - s_off[lo]) >= s_cnt[lo];
-    }
-    if (pad) {
-      if (recv_src) recv_src[s] = -1;
-      if (recv_w) recv_w[s] = 0.0f;
-    }
-  }
-}
-
-template <int BLK>
-__device__ __forceinline__ void fill_padding(int fb, const int32_t* __restrict__ off,
-                                             const int32_t* __restrict__ recv_cnt, int E,
-                                             int64_t cap, int32_t* __restrict__ recv_src,
-                                             float* __restrict__ recv_w, int* s_off, int* s_cnt) {
-  stage_offsets<BLK>(off, recv_cnt, E, s_off, s_cnt);
-  __syncthreads();
-  tag_padding((int64_t)fb * BLK * kFillPerThread, BLK, threadIdx.x, E, cap, recv_src, recv_w,
-              s_off, s_cnt);
-}
-
-// Work of a dispatch launch besides the token rows, done by the first blocks
-// of its grid so that it runs alongside them: padding tags (fill blocks),
-// zeroed padding rows (zero blocks, DeepEP's do_zero_padding) and the running
-// per-expert receive counts (one stats block, DeepEP's
-// cumulative_local_expert_recv_stats).
 struct DispatchAux {
   const int32_t* off;   // [E+1] expert region offsets
   const int32_t* cnt;   // [E] pairs per expert
@@ -650,15 +609,20 @@ struct DispatchAux {
   int64_t* stats;       // [E], or NULL
   int64_t cap;
   int E, A, row16, G;
-  int fill_blocks, zero_blocks, stat_blocks;
-  __host__ __device__ int blocks() const { return fill_blocks + zero_blocks + stat_blocks; }
+  int64_t tag_items, zero_items, stat_items;
+  __host__ __device__ int64_t items() const { return tag_items + zero_items + stat_items; }
 };
 
-// Zero blocks: wavefront v of the zero range takes padding row j = v % (A-1)
-// of expert e = v / (A-1), which exists iff j < off[e+1] - off[e] - cnt[e]
-// (an expert region has fewer than A padding rows).  Consecutive waves take
-// consecutive rows of one expert, so blocks past an expert's padding exit
-// at once.
+__device__ __forceinline__ void tag_slots(int64_t lo, int64_t hi, const DispatchAux& a) {
+  const int lane = threadIdx.x & 63;
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > a.cap ? a.cap : hi;
+  for (int64_t s = lo + lane; s < hi; s += 64) {
+    if (a.recv_src) a.recv_src[s] = -1;
+    if (a.recv_w) a.recv_w[s] = 0.0f;
+  }
+}
+
 __device__ __forceinline__ void zero_padding_row(int64_t v, const DispatchAux& a) {
   const int lane = threadIdx.x & 63;
   const int e = (int)(v / (a.A - 1)), j = (int)(v % (a.A - 1));
@@ -672,18 +636,30 @@ __device__ __forceinline__ void zero_padding_row(int64_t v, const DispatchAux& a
     for (int g = lane; g < a.G; g += 64) a.recv_scales[row * a.G + g] = 0.0f;
 }
 
+// One wavefront's auxiliary item v (0 <= v < a.items()).
+__device__ __forceinline__ void aux_item(int64_t v, const DispatchAux& a) {
+  if (v < a.tag_items) {
+    if (v < a.E) {
+      tag_slots((int64_t)a.off[v] + a.cnt[v], a.off[v + 1], a);
+    } else {
+      const int64_t lo = (v - a.E) * kTailSlots, used = a.off[a.E];
+      tag_slots(lo > used ? lo : used, lo + kTailSlots, a);
+    }
+    return;
+  }
+  v -= a.tag_items;
+  if (v < a.zero_items) {
+    zero_padding_row(v, a);
+    return;
+  }
+  for (int e = threadIdx.x & 63; e < a.E; e += 64) a.stats[e] += a.cnt[e];
+}
+
+// Blocks b >= 0 of the auxiliary range of a grid with BLK threads per block.
 template <int BLK>
-__device__ __forceinline__ void dispatch_aux(int b, const DispatchAux& a, int* s_off, int* s_cnt) {
-  if (b < a.fill_blocks) {
-    fill_padding<BLK>(b, a.off, a.cnt, a.E, a.cap, a.recv_src, a.recv_w, s_off, s_cnt);
-    return;
-  }
-  b -= a.fill_blocks;
-  if (b < a.zero_blocks) {
-    zero_padding_row((int64_t)b * (BLK / 64) + (threadIdx.x >> 6), a);
-    return;
-  }
-  for (int e = threadIdx.x; e < a.E; e += BLK) a.stats[e] += a.cnt[e];
+__device__ __forceinline__ void aux_block(int64_t b, const DispatchAux& a) {
+  const int64_t v = b * (BLK / 64) + (threadIdx.x >> 6);
+  if (v < a.items()) aux_item(v, a);
 }
 
 // Slot of pair (t, lane) for lanes < K, -1 elsewhere or when out of range.
@@ -735,36 +711,72 @@ __device__ __forceinline__ void copy_row(const u32x4* __restrict__ row,
   }
 }
 
-// bf16 rows: TPT threads (a multiple of 64) per token; NV 16-byte chunks per
-// thread per pass, so one pass moves TPT*NV*16 bytes of the row, which is read
-// once into VGPRs and then stored to each of the token's K slots.
-template <int TPT, int NV, int BLK>
-__global__ __launch_bounds__(BLK) void dispatch_bf16_kernel(
-    const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
-    u32x4* __restrict__ recv_x, int32_t* __restrict__ recv_src, float* __restrict__ recv_w,
-    int N, int K, int H8, int64_t cap, DispatchAux aux) {
-  __shared__ int s_off[EP_MAX_EXPERTS + 1];
-  __shared__ int s_cnt[EP_MAX_EXPERTS];
-  // the auxiliary blocks come first so that they run alongside the token
-  // blocks instead of after them
-  const int nb = aux.blocks();
-  if ((int)blockIdx.x < nb) {
-    dispatch_aux<BLK>(blockIdx.x, aux, s_off, s_cnt);
-    return;
+// E4M3 codes of the 16 consecutive channels this lane holds (two 16-byte
+// chunks of bf16, v0 then v1), as part of a 128-channel group held by 8
+// consecutive lanes 8j..8j+7, whose amax is reduced with xor-shuffles (all 64
+// lanes must call this).  Sets `scale` to the group's scale:
+//   amax = max |v|, scale = amax/448, inv = 448/amax (fp32 divisions),
+//   code = E4M3(v * inv), round to nearest even, saturating; an all-zero
+//   group has scale 1 and keeps each zero's sign.
+__device__ __forceinline__ u32x4 quant16(u32x4 v0, u32x4 v1, float& scale) {
+  float f[16];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    f[2 * j] = bf16_lo(v0[j]);
+    f[2 * j + 1] = bf16_hi(v0[j]);
+    f[8 + 2 * j] = bf16_lo(v1[j]);
+    f[8 + 2 * j + 1] = bf16_hi(v1[j]);
   }
-  constexpr int kTok = BLK / TPT;
-  const int t = uniform(((int)blockIdx.x - nb) * kTok + (int)(threadIdx.x / TPT));
-  if (t >= N) return;
-  const int lane = threadIdx.x & 63;
-  const int vl = threadIdx.x % TPT;
-  const int myslot = load_slot(slot_of, t, K, lane, cap);
-  copy_row<TPT, NV>(x + (int64_t)t * H8, recv_x, myslot, K, H8, vl);
-  if (vl < 64) write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(f[j]));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  am = fmaxf(am, __shfl_xor(am, 4));
+  const bool zero = (am == 0.0f);
+  scale = zero ? 1.0f : am / 448.0f;
+  float inv = 448.0f / am;
+  u32x4 q;
+  if (!zero) {
+    if (!__builtin_isfinite(inv)) {
+      // amax < 448/FLT_MAX: the inverse overflows.  The codes approximate
+      // v * 448/amax, which multiplying the whole group by 2^64 (exact for
+      // bf16 values) leaves unchanged, so the scaled group is quantised.
+      inv = 448.0f / (am * 0x1p64f);
+#pragma unroll
+      for (int j = 0; j < 16; j++) f[j] *= 0x1p64f;
+    }
+    // |f * inv| <= 448 (1 + 2^-23) < 464 here, where the hardware
+    // conversion (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even,
+    // saturating) is the contract's encoder; a GPU test compares it with the
+    // oracle's encoder on every float32 below 464 in magnitude
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float p0 = f[4 * j] * inv, p1 = f[4 * j + 1] * inv;
+      const float p2 = f[4 * j + 2] * inv, p3 = f[4 * j + 3] * inv;
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+      q[j] = (uint32_t)word;
+    }
+  } else {
+    // all-zero group: scale 1, each zero keeps its sign
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; b++) word |= ((__float_as_uint(f[4 * j + b]) >> 24) & 0x80u) << (8 * b);
+      q[j] = word;
+    }
+  }
+  return q;
 }
 
 // Quantise one bf16 row of H channels (H % 128 == 0) to E4M3 with one fp32
 // scale per 128-channel group and store codes and scales to the slots that
-// lanes 0..K-1 of `myslot` name; one wavefront per row.
+// lanes 0..K-1 of `myslot` name; one wavefront per row (the CU-budget and
+// low-latency kernels).  NI pieces of 1024 channels per pass; after piece i,
+// lanes 8i..8i+7 pick up the scales of its groups so that one store per slot
+// writes the pass's scales.
 template <int NI>
 __device__ __forceinline__ void quant_row_fp8(const u32x4* __restrict__ row,
                                               u32x4* __restrict__ recv_q,
@@ -785,55 +797,8 @@ __device__ __forceinline__ void quant_row_fp8(const u32x4* __restrict__ row,
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const int ch = pbase + i * 1024 + lane * 16;
-      float f[16];
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        f[2 * j] = bf16_lo(v[i][0][j]);
-        f[2 * j + 1] = bf16_hi(v[i][0][j]);
-        f[8 + 2 * j] = bf16_lo(v[i][1][j]);
-        f[8 + 2 * j + 1] = bf16_hi(v[i][1][j]);
-      }
-      float am = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; j++) am = fmaxf(am, fabsf(f[j]));
-      am = fmaxf(am, __shfl_xor(am, 1));
-      am = fmaxf(am, __shfl_xor(am, 2));
-      am = fmaxf(am, __shfl_xor(am, 4));
-      const bool zero = (am == 0.0f);
-      const float scale = zero ? 1.0f : am / 448.0f;
-      float inv = 448.0f / am;
-      u32x4 q;
-      if (!zero) {
-        if (!__builtin_isfinite(inv)) {
-          // amax < 448/FLT_MAX: the inverse overflows.  The codes approximate
-          // v * 448/amax, which multiplying the whole group by 2^64 (exact for
-          // bf16 values) leaves unchanged, so the scaled group is quantised.
-          inv = 448.0f / (am * 0x1p64f);
-#pragma unroll
-          for (int j = 0; j < 16; j++) f[j] *= 0x1p64f;
-        }
-        // |f * inv| <= 448 (1 + 2^-23) < 464 here, where the hardware
-        // conversion (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even,
-        // saturating) is the contract's encoder; a GPU test compares it
-        // with the oracle's encoder on every float32 below 464 in magnitude
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const float p0 = f[4 * j] * inv, p1 = f[4 * j + 1] * inv;
-          const float p2 = f[4 * j + 2] * inv, p3 = f[4 * j + 3] * inv;
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-          q[j] = (uint32_t)word;
-        }
-      } else {
-        // all-zero group: scale 1, each zero keeps its sign
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int b = 0; b < 4; b++) word |= ((__float_as_uint(f[4 * j + b]) >> 24) & 0x80u) << (8 * b);
-          q[j] = word;
-        }
-      }
+      float scale;
+      const u32x4 q = quant16(v[i][0], v[i][1], scale);
       const float sv = __shfl(scale, 8 * (lane & 7));
       if ((lane >> 3) == i) my_scale = sv;
       if (ch < H) {
@@ -855,29 +820,50 @@ __device__ __forceinline__ void quant_row_fp8(const u32x4* __restrict__ row,
   }
 }
 
-// e4m3 rows: one wavefront per token.  A lane owns 16 consecutive channels
-// (two 16-byte bf16 loads, one 16-byte code store); 8 lanes form a
-// 128-channel group whose amax is reduced with xor-shuffles.  NI iterations
-// of 1024 channels per pass.  After iteration i, lanes 8i..8i+7 pick up the
-// scales of groups 8i..8i+7 so that one store per slot writes 64 scales.
-template <int NI>
-__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
+// Fused e4m3 rows as (token, piece) items, one wavefront each: item
+// b = t * P + p quantises piece p of token t (1024 channels, 8 groups of 128,
+// 16 channels per lane) and stores its codes and 8 scales to each of the
+// token's K slots.  Measured on the e4m3 prefill workload: 48.7 us per launch
+// (152.8 us per step, 165 us from a cold cache) against 54.1 us (156.5 /
+// 167 us) for one wavefront per token walking its row piece by piece; the
+// smaller items keep more rows in flight.  Splitting an item's K slots over
+// S wavefronts that each quantise the piece again (placed on one XCD so that
+// the piece is read from HBM once) gains nothing at S = 2 and loses at S = 4
+// (158.3 / 175.3 us).  Lanes past H (when H % 1024 != 0) hold whole groups:
+// they load clamped addresses, take part in the shuffles and store nothing.
+// A launch holds at most kItemLaunch items; larger problems take several.
+constexpr int64_t kItemLaunch = 1 << 30;
+
+__global__ __launch_bounds__(64) void dispatch_fp8_item_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
     u32x4* __restrict__ recv_q, float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
-    float* __restrict__ recv_w, int N, int K, int H, int64_t cap, DispatchAux aux) {
-  __shared__ int s_off[EP_MAX_EXPERTS + 1];
-  __shared__ int s_cnt[EP_MAX_EXPERTS];
-  const int nb = aux.blocks();
-  if ((int)blockIdx.x < nb) {
-    dispatch_aux<kThreads>(blockIdx.x, aux, s_off, s_cnt);
+    float* __restrict__ recv_w, int N, int K, int H, int P, int64_t item0, int64_t items,
+    int64_t cap, DispatchAux aux) {
+  const int64_t b = item0 + blockIdx.x;
+  if (b >= items) {
+    aux_block<64>(b - items, aux);
     return;
   }
-  const int t = uniform(((int)blockIdx.x - nb) * kWaves + (threadIdx.x >> 6));
-  if (t >= N) return;
-  const int lane = threadIdx.x & 63;
+  const int t = (int)(b / P), p = (int)(b % P);
+  const int lane = threadIdx.x;
+  const int H16 = H >> 4, G = H >> 7;
+  const int ch = p * 1024 + lane * 16;
+  const int chc = ch < H ? ch : H - 16;
+  const u32x4* row = x + (int64_t)t * (H >> 3);
+  const u32x4 v0 = ld16<EP_DISPATCH_NT_LOAD>(row + (chc >> 3));
+  const u32x4 v1 = ld16<EP_DISPATCH_NT_LOAD>(row + (chc >> 3) + 1);
   const int myslot = load_slot(slot_of, t, K, lane, cap);
-  quant_row_fp8<NI>(x + (int64_t)t * (H >> 3), recv_q, recv_scales, myslot, K, H, lane);
-  write_meta(t, K, lane, myslot, w, recv_src, recv_w);
+  float scale;
+  const u32x4 q = quant16(v0, v1, scale);
+  for (int k = 0; k < K; k++) {
+    const int s = lane_value(myslot, k);
+    if (s < 0) continue;
+    if (ch < H) {
+      st16(recv_q + (int64_t)s * H16 + (ch >> 4), q);
+      if ((lane & 7) == 0) recv_scales[(int64_t)s * G + (ch >> 7)] = scale;
+    }
+  }
+  if (p == 0) write_meta(t, K, lane, myslot, w, recv_src, recv_w);
 }
 
 // The G scales of token t to each slot lanes 0..K-1 of `myslot` name.
@@ -894,29 +880,41 @@ __device__ __forceinline__ void copy_scales(const float* __restrict__ xs, int t,
   }
 }
 
-// Pre-quantised rows (DeepEP's dispatch also takes x as a pair of e4m3 codes
-// and per-128-channel scales): one wavefront per token copies the H code
-// bytes (H/16 chunks, NV per lane) and the H/128 scales to each of the
-// token's slots, unchanged.
-template <int NV>
-__global__ __launch_bounds__(kThreads) void dispatch_prequant_kernel(
-    const u32x4* __restrict__ xq, const float* __restrict__ xs, const float* __restrict__ w,
-    const int32_t* __restrict__ slot_of, u32x4* __restrict__ recv_q,
+// Token rows, one wavefront per token, kTokPerBlock per workgroup: MODE 0
+// reads a bf16 row into VGPRs once (NV 16-byte chunks per lane per pass) and
+// stores it to each of the token's K slots; MODE 2 copies pre-quantised e4m3
+// codes and their scales the same way.
+// Workgroups past the tokens do the auxiliary work, after every token block
+// has been issued.
+// Measured against (token, k, piece) workgroups ordered so that the K readers
+// of a piece share an XCD: those win when x is still in the Infinity Cache
+// (85 vs 97 us at the prefill shape) but lose badly from a cold cache (163 vs
+// 112 us), because the K concurrent reads of a piece are not merged into one
+// HBM read; windowed orders that delay the re-reads do not close the gap
+// (118 us at best).  In a real step x arrives cold, so the row is read once.
+constexpr int kTokPerBlock = kThreads / 64;
+
+template <int MODE, int NV>  // MODE 0: bf16 rows; 2: pre-quantised e4m3 rows + scales
+__global__ __launch_bounds__(kThreads) void dispatch_token_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ xs, const float* __restrict__ w,
+    const int32_t* __restrict__ slot_of, u32x4* __restrict__ recv_x,
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src, float* __restrict__ recv_w,
     int N, int K, int H, int64_t cap, DispatchAux aux) {
-  __shared__ int s_off[EP_MAX_EXPERTS + 1];
-  __shared__ int s_cnt[EP_MAX_EXPERTS];
-  const int nb = aux.blocks();
-  if ((int)blockIdx.x < nb) {
-    dispatch_aux<kThreads>(blockIdx.x, aux, s_off, s_cnt);
+  const int tok_blocks = (N + kTokPerBlock - 1) / kTokPerBlock;
+  if ((int)blockIdx.x >= tok_blocks) {
+    aux_block<kThreads>((int64_t)blockIdx.x - tok_blocks, aux);
     return;
   }
-  const int t = uniform(((int)blockIdx.x - nb) * kWaves + (threadIdx.x >> 6));
+  const int t = uniform((int)blockIdx.x * kTokPerBlock + (int)(threadIdx.x >> 6));
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
-  copy_row<64, NV>(xq + (int64_t)t * (H >> 4), recv_q, myslot, K, H >> 4, lane);
-  copy_scales(xs, t, H >> 7, recv_scales, myslot, K, lane);
+  if constexpr (MODE == 0) {
+    copy_row<64, NV>(x + (int64_t)t * (H >> 3), recv_x, myslot, K, H >> 3, lane);
+  } else {
+    copy_row<64, NV>(x + (int64_t)t * (H >> 4), recv_x, myslot, K, H >> 4, lane);
+    copy_scales(xs, t, H >> 7, recv_scales, myslot, K, lane);
+  }
   write_meta(t, K, lane, myslot, w, recv_src, recv_w);
 }
 
@@ -926,12 +924,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_prequant_kernel(
 // workgroups of 1024 threads, each reserving all of a CU's LDS (160 KiB on
 // gfx950), so that no CU holds two of them, nor any other workgroup that uses
 // LDS (a GEMM's): the kernel occupies min(budget, work) CUs alone and leaves
-// the rest to other streams.  Its 16
-// wavefronts take work items i = blockIdx.x*16 + wave, stepping by
-// gridDim.x*16; an item is one token row (dispatch), one token's 64-chunk
-// column group (combine), or one piece of the auxiliary work: tags for 512
-// slots, one candidate padding row, or the statistics.  Every item runs the
-// same wavefront code as the ordinary grids, so results are identical.
+// the rest to other streams.  Its 16 wavefronts take work items
+// i = blockIdx.x*16 + wave, stepping by gridDim.x*16; an item is one token
+// row (dispatch), one token's 64-chunk column group (combine), or one item of
+// the auxiliary work (aux_item).  Every item runs the same wavefront code as
+// the wavefront-per-token paths, so results are identical.
 constexpr int kPersistThreads = 1024;
 constexpr int kPersistWaves = kPersistThreads / 64;
 constexpr int kCombinePersistNV = 2;  // 16-byte chunks per lane per combine item
@@ -941,33 +938,19 @@ __global__ __launch_bounds__(kPersistThreads) void dispatch_persist_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ xs, const float* __restrict__ w,
     const int32_t* __restrict__ slot_of, u32x4* __restrict__ recv_x,
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src, float* __restrict__ recv_w,
-    int N, int K, int H, int64_t cap, DispatchAux aux, int64_t fill_items, int64_t zero_items) {
-  extern __shared__ int lds[];  // [E+1] offsets, [E] counts; the rest only reserves the CU
-  int* s_off = lds;
-  int* s_cnt = lds + aux.E + 1;
-  if (fill_items > 0) stage_offsets<kPersistThreads>(aux.off, aux.cnt, aux.E, s_off, s_cnt);
-  __syncthreads();
+    int N, int K, int H, int64_t cap, DispatchAux aux) {
+  extern __shared__ int lds[];  // only reserves the CU
+  if (N < 0) lds[threadIdx.x] = 0;
   const int lane = threadIdx.x & 63;
-  const int64_t stat_items = aux.stats ? 1 : 0;
-  const int64_t n_items = fill_items + zero_items + stat_items + N;
+  const int64_t n_aux = aux.items();
+  const int64_t n_items = n_aux + N;
   for (int64_t i = (int64_t)blockIdx.x * kPersistWaves + (threadIdx.x >> 6); i < n_items;
        i += (int64_t)gridDim.x * kPersistWaves) {
-    int64_t r = i;
-    if (r < fill_items) {
-      tag_padding(r * 64 * kFillPerThread, 64, lane, aux.E, cap, recv_src, recv_w, s_off, s_cnt);
+    if (i < n_aux) {
+      aux_item(i, aux);
       continue;
     }
-    r -= fill_items;
-    if (r < zero_items) {
-      zero_padding_row(r, aux);
-      continue;
-    }
-    r -= zero_items;
-    if (r < stat_items) {
-      for (int e = lane; e < aux.E; e += 64) aux.stats[e] += aux.cnt[e];
-      continue;
-    }
-    const int t = uniform((int)(r - stat_items));
+    const int t = uniform((int)(i - n_aux));
     const int myslot = load_slot(slot_of, t, K, lane, cap);
     if constexpr (MODE == 0) {
       copy_row<64, NV>(x + (int64_t)t * (H >> 3), recv_x, myslot, K, H >> 3, lane);
@@ -1461,41 +1444,31 @@ Plan make_plan(const ep_problem_t* p) {
   return pl;
 }
 
-template <int NV>
-void launch_dispatch_bf16(int grid, hipStream_t st, const ep_problem_t* p,
-                          const ep_dispatch_args_t* a, const DispatchAux& aux) {
-  constexpr int blk = EP_DISPATCH_TPT > kThreads ? EP_DISPATCH_TPT : kThreads;
-  dispatch_bf16_kernel<EP_DISPATCH_TPT, NV, blk><<<grid, blk, 0, st>>>(
-      (const u32x4*)a->x, a->topk_weights, a->slot_of, (u32x4*)a->recv_x, a->recv_src_idx,
-      a->recv_topk_weights, p->num_tokens, p->num_topk, p->hidden / 8, a->recv_capacity, aux);
-}
-
-template <int NI>
-void launch_dispatch_fp8(int grid, hipStream_t st, const ep_problem_t* p,
-                         const ep_dispatch_args_t* a, const DispatchAux& aux) {
-  dispatch_fp8_kernel<NI><<<grid, kThreads, 0, st>>>(
-      (const u32x4*)a->x, a->topk_weights, a->slot_of, (u32x4*)a->recv_x, a->recv_scales,
-      a->recv_src_idx, a->recv_topk_weights, p->num_tokens, p->num_topk, p->hidden,
-      a->recv_capacity, aux);
-}
-
-template <int NV>
-void launch_dispatch_prequant(int grid, hipStream_t st, const ep_problem_t* p,
-                              const ep_dispatch_args_t* a, const DispatchAux& aux) {
-  dispatch_prequant_kernel<NV><<<grid, kThreads, 0, st>>>(
+template <int MODE, int NV>
+void launch_dispatch_token(int grid, hipStream_t st, const ep_problem_t* p,
+                           const ep_dispatch_args_t* a, const DispatchAux& aux) {
+  dispatch_token_kernel<MODE, NV><<<grid, kThreads, 0, st>>>(
       (const u32x4*)a->x, a->x_scales, a->topk_weights, a->slot_of, (u32x4*)a->recv_x,
       a->recv_scales, a->recv_src_idx, a->recv_topk_weights, p->num_tokens, p->num_topk,
       p->hidden, a->recv_capacity, aux);
 }
 
+void launch_dispatch_fp8_item(int grid, hipStream_t st, const ep_problem_t* p,
+                              const ep_dispatch_args_t* a, const DispatchAux& aux, int P,
+                              int64_t item0, int64_t items) {
+  dispatch_fp8_item_kernel<<<grid, 64, 0, st>>>(
+      (const u32x4*)a->x, a->topk_weights, a->slot_of, (u32x4*)a->recv_x, a->recv_scales,
+      a->recv_src_idx, a->recv_topk_weights, p->num_tokens, p->num_topk, p->hidden, P, item0,
+      items, a->recv_capacity, aux);
+}
+
 template <int MODE, int NV>
-void launch_dispatch_persist(int grid, hipStream_t st, const ep_problem_t* p,
-                             const ep_dispatch_args_t* a, const DispatchAux& aux,
-                             int64_t fill_items, int64_t zero_items) {
-  dispatch_persist_kernel<MODE, NV><<<grid, kPersistThreads, persist_lds(), st>>>(
+void launch_dispatch_persist(int grid, size_t lds, hipStream_t st, const ep_problem_t* p,
+                             const ep_dispatch_args_t* a, const DispatchAux& aux) {
+  dispatch_persist_kernel<MODE, NV><<<grid, kPersistThreads, lds, st>>>(
       (const u32x4*)a->x, a->x_scales, a->topk_weights, a->slot_of, (u32x4*)a->recv_x,
       a->recv_scales, a->recv_src_idx, a->recv_topk_weights, p->num_tokens, p->num_topk,
-      p->hidden, a->recv_capacity, aux, fill_items, zero_items);
+      p->hidden, a->recv_capacity, aux);
 }
 
 // Layout launches for one index type.
@@ -1715,17 +1688,9 @@ int ep_dispatch_ex(const ep_problem_t* p, const ep_dispatch_args_t* a, void* str
   if (zero && (!a->recv_x || (p->use_fp8 && !a->recv_scales))) return EP_ERR_INVALID_ARG;
   rc = check_device();
   if (rc != EP_OK) return rc;
-  constexpr int dblk = EP_DISPATCH_TPT > kThreads ? EP_DISPATCH_TPT : kThreads;
-  const int tok_per_block = p->use_fp8 ? kWaves : dblk / EP_DISPATCH_TPT;
-  const int blk = p->use_fp8 ? kThreads : dblk;
-  const int64_t tok_blocks = (N + tok_per_block - 1) / tok_per_block;
-  const int64_t fill_slots = (int64_t)blk * kFillPerThread;
-  const int64_t fill_blocks = meta ? (cap + fill_slots - 1) / fill_slots : 0;
-  const int64_t zero_waves = zero ? (int64_t)E * (A - 1) : 0;
-  const int64_t zero_blocks = (zero_waves + blk / 64 - 1) / (blk / 64);
-  const int64_t grid = tok_blocks + fill_blocks + zero_blocks + (stats ? 1 : 0);
-  if (grid > INT32_MAX) return EP_ERR_INVALID_ARG;
-  if (grid == 0) return EP_OK;
+  const int K = p->num_topk;
+  const int mode = prequant ? 2 : (p->use_fp8 ? 1 : 0);  // 0 bf16, 1 fused e4m3, 2 pre-quantised
+  // the work besides the token rows, as wavefront items (aux_item)
   DispatchAux aux{};
   aux.off = a->expert_slot_offset;
   aux.cnt = a->num_recv_per_expert;
@@ -1739,24 +1704,24 @@ int ep_dispatch_ex(const ep_problem_t* p, const ep_dispatch_args_t* a, void* str
   aux.A = A;
   aux.row16 = p->use_fp8 ? H / 16 : H / 8;
   aux.G = p->use_fp8 ? H / 128 : 0;
-  aux.fill_blocks = (int)fill_blocks;
-  aux.zero_blocks = (int)zero_blocks;
-  aux.stat_blocks = stats ? 1 : 0;
+  aux.tag_items = meta ? E + (cap + kTailSlots - 1) / kTailSlots : 0;
+  aux.zero_items = zero ? (int64_t)E * (A - 1) : 0;
+  aux.stat_items = stats ? 1 : 0;
+  const int64_t n_aux = aux.items();
+  // 16-byte chunks per lane of one wavefront-per-row pass (1024 channels for e4m3)
+  const int q = mode == 0 ? (H / 8 + 63) / 64 : (mode == 2 ? (H / 16 + 63) / 64 : (H + 1023) / 1024);
   hipStream_t st = (hipStream_t)stream;
   if (p->cu_budget > 0) {
     // persistent grid: one 1024-thread workgroup per CU, wavefront work items
-    const int64_t fill_items = meta ? (cap + 64 * kFillPerThread - 1) / (64 * kFillPerThread) : 0;
-    const int64_t items = N + fill_items + zero_waves + (stats ? 1 : 0);
-    const int64_t want = (items + kPersistWaves - 1) / kPersistWaves;
+    const int64_t n_items = N + n_aux;
+    const int64_t want = (n_items + kPersistWaves - 1) / kPersistWaves;
     const int pg = (int)(want < p->cu_budget ? want : p->cu_budget);
     if (pg == 0) return EP_OK;
     const size_t lds = persist_lds();
     EP_LOG("dispatch (CU budget %d) N=%d H=%d K=%d cap=%lld: workgroups=%d items=%lld lds=%zu",
-           p->cu_budget, N, H, p->num_topk, (long long)cap, pg, (long long)items, lds);
-    if (lds < 4 * (2 * (size_t)EP_MAX_EXPERTS + 1)) return EP_ERR_HIP;
-    const int mode = prequant ? 2 : (p->use_fp8 ? 1 : 0);
-    const int q = mode == 0 ? (H / 8 + 63) / 64 : (mode == 2 ? (H / 16 + 63) / 64 : (H + 1023) / 1024);
-#define EP_DP(M, NV) launch_dispatch_persist<M, NV>(pg, st, p, a, aux, fill_items, zero_waves)
+           p->cu_budget, N, H, K, (long long)cap, pg, (long long)n_items, lds);
+    if (lds == 0) return EP_ERR_HIP;
+#define EP_DP(M, NV) launch_dispatch_persist<M, NV>(pg, lds, st, p, a, aux)
     if (mode == 0) {
       if (q <= 1) EP_DP(0, 1);
       else if (q <= 2) EP_DP(0, 2);
@@ -1782,42 +1747,51 @@ int ep_dispatch_ex(const ep_problem_t* p, const ep_dispatch_args_t* a, void* str
 #undef EP_DP
     return check_launch("dispatch_persist");
   }
-  EP_LOG("dispatch %s N=%d H=%d K=%d cap=%lld: token blocks=%lld fill=%lld zero=%lld stats=%d",
-         prequant ? "pre-quantised e4m3" : (p->use_fp8 ? "e4m3" : "bf16"), N, H, p->num_topk,
-         (long long)cap, (long long)tok_blocks, (long long)fill_blocks, (long long)zero_blocks,
-         (int)stats);
-  const int g = (int)grid;
-  if (prequant) {
-    const int q = (H / 16 + 63) / 64;
-#define EP_DQ(NV) launch_dispatch_prequant<NV>(g, st, p, a, aux)
-    if (q <= 1) EP_DQ(1);
-    else if (q <= 2) EP_DQ(2);
-    else if (q <= 4) EP_DQ(4);
-    else if (q <= 7) EP_DQ(7);
-    else if (q <= 8) EP_DQ(8);
-    else EP_DQ(16);
-#undef EP_DQ
-  } else if (!p->use_fp8) {
-    const int q = (H / 8 + EP_DISPATCH_TPT - 1) / EP_DISPATCH_TPT;
-#define EP_D16(NV) launch_dispatch_bf16<NV>(g, st, p, a, aux)
-    if (q <= 1) EP_D16(1);
-    else if (q <= 2) EP_D16(2);
-    else if (q <= 4) EP_D16(4);
-    else if (q <= 7) EP_D16(7);
-    else if (q <= 8) EP_D16(8);
-    else if (q <= 14) EP_D16(14);
-    else EP_D16(16);
-#undef EP_D16
-  } else {
-    const int q = (H + 1023) / 1024;
-#define EP_D8(NI) launch_dispatch_fp8<NI>(g, st, p, a, aux)
-    if (q <= 1) EP_D8(1);
-    else if (q <= 2) EP_D8(2);
-    else if (q <= 4) EP_D8(4);
-    else if (q <= 7) EP_D8(7);
-    else EP_D8(8);
-#undef EP_D8
+  if (mode == 1) {
+    // fused e4m3: (token, 1024-channel piece) items of one wavefront, then
+    // the auxiliary blocks
+    const int P = (H + 1023) / 1024;
+    const int64_t items = (int64_t)N * P;
+    if (items + n_aux == 0) return EP_OK;
+    EP_LOG("dispatch e4m3 N=%d H=%d K=%d cap=%lld: items=%lld (pieces %d) aux items=%lld", N, H,
+           K, (long long)cap, (long long)items, P, (long long)n_aux);
+    for (int64_t item0 = 0;; item0 += kItemLaunch) {
+      const int64_t left = items - item0;
+      const bool last = left <= kItemLaunch;
+      const int64_t grid = last ? left + n_aux : kItemLaunch;
+      if (grid > INT32_MAX) return EP_ERR_INVALID_ARG;
+      launch_dispatch_fp8_item((int)grid, st, p, a, aux, P, item0, items);
+      if ((rc = check_launch("dispatch")) != EP_OK || last) return rc;
+    }
   }
+  // row copies: one wavefront per token, then the auxiliary blocks
+  const int64_t grid = ((int64_t)N + kTokPerBlock - 1) / kTokPerBlock +
+                       (n_aux + kTokPerBlock - 1) / kTokPerBlock;
+  if (grid > INT32_MAX) return EP_ERR_INVALID_ARG;
+  if (grid == 0) return EP_OK;
+  EP_LOG("dispatch %s N=%d H=%d K=%d cap=%lld: token blocks=%d aux items=%lld (tags %lld, "
+         "zero rows %lld, stats %lld)", prequant ? "pre-quantised e4m3" : "bf16", N, H, K,
+         (long long)cap, (N + kTokPerBlock - 1) / kTokPerBlock, (long long)n_aux,
+         (long long)aux.tag_items, (long long)aux.zero_items, (long long)aux.stat_items);
+  const int g = (int)grid;
+#define EP_DT(M, NV) launch_dispatch_token<M, NV>(g, st, p, a, aux)
+  if (mode == 0) {
+    if (q <= 1) EP_DT(0, 1);
+    else if (q <= 2) EP_DT(0, 2);
+    else if (q <= 4) EP_DT(0, 4);
+    else if (q <= 7) EP_DT(0, 7);
+    else if (q <= 8) EP_DT(0, 8);
+    else if (q <= 14) EP_DT(0, 14);
+    else EP_DT(0, 16);
+  } else {
+    if (q <= 1) EP_DT(2, 1);
+    else if (q <= 2) EP_DT(2, 2);
+    else if (q <= 4) EP_DT(2, 4);
+    else if (q <= 7) EP_DT(2, 7);
+    else if (q <= 8) EP_DT(2, 8);
+    else EP_DT(2, 16);
+  }
+#undef EP_DT
   return check_launch("dispatch");
 }
 

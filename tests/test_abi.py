@@ -237,3 +237,21 @@ def test_binding_offers_every_entry_point_by_its_c_name():
         if fn == "ep_status_str":
             continue   # raised as the message of EPError
         assert callable(getattr(ep, fn, None)), fn
+
+
+def test_c_shaped_wrappers_pass_the_structs_through():
+    """ep_dispatch_ex / ep_ll_dispatch_ex in Python are the C calls with their
+    own argument structs; host validation errors come back as EPError."""
+    p = _p()
+    a = ep.DispatchArgs()
+    a.recv_capacity = 10 ** 6          # no payload pointers: rejected before any launch
+    with pytest.raises(ep.EPError) as ex:
+        ep.ep_dispatch_ex(p, a, stream=0)
+    assert ex.value.code == 1
+    a.recv_capacity = 1                # below N*K + E*(A-1)
+    with pytest.raises(ep.EPError) as ex:
+        ep.ep_dispatch_ex(p, a, stream=0)
+    assert ex.value.code == 2
+    with pytest.raises(ep.EPError) as ex:
+        ep.ep_ll_dispatch_ex(p, 8, ep.LLArgs(), stream=0)
+    assert ex.value.code == 1
