@@ -1117,19 +1117,10 @@ __global__ __launch_bounds__(kThreads) void ll_empty_kernel(int32_t* __restrict_
 }
 
 // ---------------------------------------------------------------- combine
-// Combine: TPT threads (a multiple of 64) per token, one 16-byte chunk per
-// thread per pass.  The rows of the token's pairs are loaded, then
-// accumulated in ascending k: acc = acc + w_k * row_k (separately rounded
-// multiply and add, matching the contract bit for bit), and stored as bf16
-// with round-to-nearest-even (v_cvt_pk_bf16_f32).
-//
-// The launch picks TPT so that a row is covered in one pass whenever it fits
-// in 16 wavefronts (896 threads at hidden 7168): every expert row of the token
-// is then requested as a whole, at once.  Measured on MI355X this matters far
-// more than arithmetic, which the memory time hides completely: one wavefront
-// walking 1 KiB pieces of the K rows reaches ~5.2 TB/s, whole rows ~5.8 TB/s.
-// Wider rows take several passes, software-pipelined for K <= 8 (pass i+1's
-// loads in flight while pass i is accumulated).  Loads are branch-free (the
+// Combine: the K expert rows of a token are gathered and accumulated in
+// ascending k, acc = acc + w_k * row_k (separately rounded multiply and add,
+// matching the contract bit for bit), and stored as bf16 with
+// round-to-nearest-even (v_cvt_pk_bf16_f32).  Loads are branch-free (the
 // column index is clamped and invalid slots read row 0); only the
 // accumulation skips slots that hold no pair.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -1202,49 +1193,84 @@ __device__ __forceinline__ void combine_pass8(const u32x4 (&v)[8][NV], int myslo
   combine_store<TPT, NV>(acc, yrow, base, vl, H8);
 }
 
-template <int TPT, int BLK, bool MULTI>
-__global__ __launch_bounds__(BLK) void combine_kernel(
+// The ordinary launch takes (token, piece) items, one wavefront each: item
+// b = t * P + p reduces piece p of the token's rows (64 16-byte chunks, one
+// per lane), with all K (or the next 8 of K) rows of the piece requested
+// before any is used.  Measured on MI355X at hidden 7168: 85.9 us at the
+// prefill shape and 20.1 us at the decode shape, against 88.8 / 23.2 us for
+// one 896-thread workgroup per token (the whole rows requested at once) and
+// 101 us for one wavefront walking the pieces of its token in turn; the
+// reads dominate (eight rows read per row written), and many small
+// independent items keep the most of them in flight.  Any row width is P
+// pieces; K > 8 goes through groups of 8 rows, accumulated group after group
+// so that the order over k is kept.
+// KT = K (1..8): the token's slots and weights are uniform loads (scalar) that
+// arrive together, so the row loads can all be issued after one wait.
+template <int KT>
+__global__ __launch_bounds__(64) void combine_piece_k_kernel(
     const u32x4* __restrict__ eo, const int32_t* __restrict__ slot_of,
-    const float* __restrict__ w, u32x4* __restrict__ y, int N, int K, int H8, int64_t cap) {
-  constexpr int kTok = BLK / TPT;
-  constexpr int kStep = TPT;  // one 16-byte chunk per thread per pass
-  const int t = uniform(blockIdx.x * kTok + (int)(threadIdx.x / TPT));
+    const float* __restrict__ w, u32x4* __restrict__ y, int N, int H8, int P, int64_t item0,
+    int64_t cap) {
+  const int64_t b = item0 + blockIdx.x;
+  const int t = (int)(b / P), base = (int)(b % P) * 64;
   if (t >= N) return;
-  const int lane = threadIdx.x & 63;
-  const int vl = threadIdx.x % TPT;
+  const int lane = threadIdx.x;
+  int s[KT];
+  float wk[KT];
+#pragma unroll
+  for (int k = 0; k < KT; k++) {
+    s[k] = slot_of[(int64_t)t * KT + k];
+    wk[k] = w[(int64_t)t * KT + k];
+    if (s[k] < 0 || (int64_t)s[k] >= cap) s[k] = -1;
+  }
+  const int c = base + lane;
+  const int cc = c < H8 ? c : H8 - 1;
+  u32x4 v[KT];
+#pragma unroll
+  for (int k = 0; k < KT; k++)
+    v[k] = ld16<EP_COMBINE_NT_LOAD>(eo + (int64_t)(s[k] < 0 ? 0 : s[k]) * H8 + cc);
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc[j] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KT; k++) {
+    if (s[k] < 0) continue;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      acc[2 * q] = acc[2 * q] + wk[k] * bf16_lo(v[k][q]);
+      acc[2 * q + 1] = acc[2 * q + 1] + wk[k] * bf16_hi(v[k][q]);
+    }
+  }
+  if (c < H8) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; q++) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    st16(y + (int64_t)t * H8 + c, o);
+  }
+}
+
+// Any K (used for K > 8): slots per lane, groups of 8 rows.
+__global__ __launch_bounds__(64) void combine_piece_kernel(
+    const u32x4* __restrict__ eo, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ w, u32x4* __restrict__ y, int N, int K, int H8, int P, int64_t item0,
+    int64_t cap) {
+  const int64_t b = item0 + blockIdx.x;
+  const int t = (int)(b / P), base = (int)(b % P) * 64;
+  if (t >= N) return;
+  const int lane = threadIdx.x;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
   const float myw = (lane < K) ? w[(int64_t)t * K + lane] : 0.0f;
-  u32x4* yrow = y + (int64_t)t * H8;
-  if (MULTI && K <= 8) {
-    u32x4 va[8][1], vb[8][1];
-    combine_load8<TPT, 1>(va, eo, myslot, K, 0, vl, H8);
-    for (int base = 0; base < H8; base += 2 * kStep) {
-      const int b1 = base + kStep;
-      if (b1 < H8) combine_load8<TPT, 1>(vb, eo, myslot, K, b1, vl, H8);
-      combine_pass8<TPT, 1>(va, myslot, myw, K, yrow, base, vl, H8);
-      if (b1 >= H8) break;
-      const int b2 = b1 + kStep;
-      if (b2 < H8) combine_load8<TPT, 1>(va, eo, myslot, K, b2, vl, H8);
-      combine_pass8<TPT, 1>(vb, myslot, myw, K, yrow, b1, vl, H8);
-    }
-    return;
-  }
-  // one pass when H8 <= TPT; K > 8 goes through groups of 8 rows, accumulated
-  // group after group so that the order over k is kept
-  for (int base = 0; base < H8; base += kStep) {
-    float acc[1][8];
+  float acc[1][8];
 #pragma unroll
-    for (int j = 0; j < 8; j++) acc[0][j] = 0.0f;
-    for (int kg = 0; kg < K; kg += 8) {
-      u32x4 v[8][1];
-      const int rem = K - kg;
-      const int slot_g = __shfl_down(myslot, kg);  // lane j now holds pair kg+j
-      const float w_g = __shfl_down(myw, kg);
-      combine_load8<TPT, 1>(v, eo, slot_g, rem, base, vl, H8);
-      combine_accum8<1>(acc, v, slot_g, w_g, rem);
-    }
-    combine_store<TPT, 1>(acc, yrow, base, vl, H8);
+  for (int j = 0; j < 8; j++) acc[0][j] = 0.0f;
+  for (int kg = 0; kg < K; kg += 8) {
+    u32x4 v[8][1];
+    const int slot_g = __shfl_down(myslot, kg);  // lane j now holds pair kg + j
+    const float w_g = __shfl_down(myw, kg);
+    combine_load8<64, 1>(v, eo, slot_g, K - kg, base, lane, H8);
+    combine_accum8<1>(acc, v, slot_g, w_g, K - kg);
   }
+  combine_store<64, 1>(acc, y + (int64_t)t * H8, base, lane, H8);
 }
 
 // Combine under a CU budget (see dispatch_persist_kernel): an item is one
@@ -1514,42 +1540,6 @@ int run_layout(const ep_problem_t* p, const I* topk_idx, int32_t* num_tokens_per
       num_recv_per_expert, expert_slot_offset, slot_of, K, E, R, T, pl.CB, pl.C, pl.B,
       p->expert_alignment);
   return check_launch("layout_assign");
-}
-
-template <int Q, bool MULTI>
-void launch_combine_q(int N, hipStream_t st, const void* eo, const int32_t* slot_of,
-                      const float* w, void* y, int K, int H8, int64_t cap) {
-  constexpr int TPT = 64 * Q;
-  constexpr int BLK = TPT >= 256 ? TPT : 256;
-  constexpr int tok = BLK / TPT;
-  const int blocks = (N + tok - 1) / tok;
-  combine_kernel<TPT, BLK, MULTI><<<blocks, BLK, 0, st>>>((const u32x4*)eo, slot_of, w,
-                                                          (u32x4*)y, N, K, H8, cap);
-}
-
-void launch_combine(int q, int N, hipStream_t st, const void* eo, const int32_t* slot_of,
-                    const float* w, void* y, int K, int H8, int64_t cap) {
-#define EP_CQ(Q) launch_combine_q<Q, false>(N, st, eo, slot_of, w, y, K, H8, cap)
-  switch (q) {
-    case 1: EP_CQ(1); break;
-    case 2: EP_CQ(2); break;
-    case 3:
-    case 4: EP_CQ(4); break;
-    case 5: EP_CQ(5); break;
-    case 6: EP_CQ(6); break;
-    case 7: EP_CQ(7); break;
-    case 8: EP_CQ(8); break;
-    case 9: EP_CQ(9); break;
-    case 10: EP_CQ(10); break;
-    case 11: EP_CQ(11); break;
-    case 12: EP_CQ(12); break;
-    case 13: EP_CQ(13); break;
-    case 14: EP_CQ(14); break;
-    case 15: EP_CQ(15); break;
-    case 16: EP_CQ(16); break;
-    default: launch_combine_q<16, true>(N, st, eo, slot_of, w, y, K, H8, cap); break;
-  }
-#undef EP_CQ
 }
 
 template <int MODE, int NV>
@@ -1871,10 +1861,35 @@ int ep_combine(const ep_problem_t* p, const void* expert_out, const int32_t* slo
         recv_capacity);
     return check_launch("combine_persist");
   }
-  EP_LOG("combine N=%d H=%d K=%d cap=%lld: waves per token=%d%s", N, p->hidden, p->num_topk,
-         (long long)recv_capacity, q > 16 ? 16 : (q == 3 ? 4 : q), q > 16 ? " (multi-pass)" : "");
-  launch_combine(q, N, st, expert_out, slot_of, topk_weights, y, p->num_topk, H8, recv_capacity);
-  return check_launch("combine");
+  // (token, piece) items; a launch holds at most kItemLaunch of them
+  const int64_t items = (int64_t)N * q;
+  EP_LOG("combine N=%d H=%d K=%d cap=%lld: items=%lld (pieces %d)", N, p->hidden, p->num_topk,
+         (long long)recv_capacity, (long long)items, q);
+  for (int64_t item0 = 0; item0 < items; item0 += kItemLaunch) {
+    const int64_t left = items - item0;
+    const int grid = (int)(left < kItemLaunch ? left : kItemLaunch);
+    const u32x4* eo = (const u32x4*)expert_out;
+    u32x4* yy = (u32x4*)y;
+#define EP_CK(KK) combine_piece_k_kernel<KK><<<grid, 64, 0, st>>>(eo, slot_of, topk_weights, yy, N, \
+                                                                  H8, q, item0, recv_capacity)
+    switch (p->num_topk) {
+      case 1: EP_CK(1); break;
+      case 2: EP_CK(2); break;
+      case 3: EP_CK(3); break;
+      case 4: EP_CK(4); break;
+      case 5: EP_CK(5); break;
+      case 6: EP_CK(6); break;
+      case 7: EP_CK(7); break;
+      case 8: EP_CK(8); break;
+      default:
+        combine_piece_kernel<<<grid, 64, 0, st>>>(eo, slot_of, topk_weights, yy, N, p->num_topk,
+                                                  H8, q, item0, recv_capacity);
+        break;
+    }
+#undef EP_CK
+    if ((rc = check_launch("combine")) != EP_OK) return rc;
+  }
+  return EP_OK;
 }
 
 int64_t ep_ll_capacity(const ep_problem_t* p, int32_t max_tokens_per_rank) {
