@@ -1275,7 +1275,7 @@ __global__ __launch_bounds__(64) void combine_piece_kernel(
 
 // Combine under a CU budget (see dispatch_persist_kernel): an item is one
 // token's group of 64*NV 16-byte chunks (NV per lane); K rows of it are
-// gathered and reduced in ascending k exactly as in combine_kernel.
+// gathered and reduced in ascending k exactly as in combine_piece_kernel.
 template <int NV>
 __global__ __launch_bounds__(kPersistThreads) void combine_persist_kernel(
     const u32x4* __restrict__ eo, const int32_t* __restrict__ slot_of,
@@ -1309,7 +1309,7 @@ __global__ __launch_bounds__(kPersistThreads) void combine_persist_kernel(
 // Combine under a CU budget for rows of at most 16 wavefronts (H8 <= 1024)
 // and K <= 8: one workgroup of 64*Q threads per CU takes tokens
 // t = blockIdx.x, t + gridDim.x, ...; each thread owns one 16-byte chunk
-// column of the row, as in combine_kernel, and gathers the next token's K
+// column of the row, and gathers the next token's K
 // rows while it reduces the current one, so two tokens' rows are in flight.
 template <int Q>
 __global__ __launch_bounds__(64 * Q) void combine_persist_tok_kernel(
