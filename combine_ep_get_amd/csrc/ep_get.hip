@@ -398,6 +398,14 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
   }
 }
 
+// floor(n / d) as the high half of n * ceil(2^32 / d): exact whenever
+// n * d <= 2^32 (the error of the product is below n / 2^32 <= 1 / d, less than
+// the distance from n / d to the next integer).  magic_of is the host side.
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint64_t magic) {
+  return (uint32_t)(((uint64_t)n * magic) >> 32);
+}
+inline uint64_t magic_of(uint32_t d) { return ((uint64_t(1) << 32) + d - 1) / d; }
+
 // Single-launch layout for problems with N*K <= kFusedMaxPairs, N <= kFlagBytes
 // and E <= kFusedMaxExperts (the decode-sized workloads).
 // No block needs another block's results: each block reads all N*K routing
@@ -410,10 +418,11 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
 // LDS (N bytes at most), so the first block of a source also counts its rank
 // row.  Then the padded scan, publishing and stable ranks run as in phase 2.
 // Problems up to this many (token, k) pairs take the single-launch layout
-// (measured on MI355X: 5.0 us at 256 pairs, 6.7 us at 8192, 10.8 us at 32768,
-// where the two-launch layout costs 10.2-10.5 us throughout).
+// (measured on MI355X: 5.2 us at 288 pairs, 6.7 us at 8192, 7.6 us at 16384,
+// 10.2 us at 32768 and 16.1 us at 65536, where the two-launch layout costs
+// 10.0-10.8 us up to 32768 pairs and 11.7 us at 65536).
 #ifndef EP_FUSED_MAX_PAIRS
-#define EP_FUSED_MAX_PAIRS 16384
+#define EP_FUSED_MAX_PAIRS 32768
 #endif
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedMaxPairs = EP_FUSED_MAX_PAIRS;
@@ -424,14 +433,13 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
     const I* __restrict__ topk_idx, uint8_t* __restrict__ in_rank,
     int32_t* __restrict__ err_word, int32_t* __restrict__ num_tokens_per_rank,
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ num_recv,
-    int32_t* __restrict__ off, int32_t* __restrict__ slot_of, int N, int K, int E, int R, int L,
-    int T, int CB, int C, int A) {
+    int32_t* __restrict__ off, int32_t* __restrict__ slot_of, int N, int K, int E, int R, int T,
+    int CB, int C, int A, uint64_t magic_k, uint64_t magic_l) {
   constexpr int BLK = kFusedThreads;
   constexpr int kWv = BLK / 64;
   __shared__ int sidx[kAssignTile];
   __shared__ int hist[4][kFusedMaxExperts];
   __shared__ int base[kFusedMaxExperts];
-  __shared__ short srank[kFusedMaxExperts];
   __shared__ int rsum[EP_MAX_RANKS];
   __shared__ uint32_t flagw[kFlagBytes / 4];
   __shared__ int wsum[kWv];
@@ -449,14 +457,15 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
   load_idx<BLK, kAssignTile>(iv, topk_idx + p0, np);
   for (int q = tid; q < 4 * E; q += BLK) (&hist[0][0])[(q / E) * kFusedMaxExperts + q % E] = 0;
   for (int q = tid; q < (T * R + 3) / 4; q += BLK) flagw[q] = 0u;
-  for (int e = tid; e < E; e += BLK) srank[e] = (short)(e / L);
   if (tid == 0) err = 0;
   __syncthreads();
   store_idx<BLK, kAssignTile>(sidx, iv, np);
 
   // (a) every pair of the problem, 16 loads in flight per thread; the class
   //     comes from comparing the pair's position with the (token-aligned)
-  //     class boundaries, the expert -> rank map from an LDS table
+  //     class boundaries.  Token and rank of a pair of the block's source come
+  //     from multiplications (div_magic), so the loop reads no LDS and issues
+  //     its LDS atomics and flag stores without waiting on any of them.
   const int NK = N * K, ps0 = src * T * K, ps1 = ps0 + T * K;
   for (int pb = 0; pb < NK; pb += 16 * BLK) {
     int v[16];
@@ -467,10 +476,11 @@ __global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
       const int p = pb + u * BLK + tid;
       const int e = v[u];
       if (p < NK) {
-        if (e >= 0 && e < E) {
+        if ((unsigned)e < (unsigned)E) {
           const int cls = (p >= ps0) + (p >= p0) + (p >= ps1);
           atomicAdd(&hist[cls][e], 1);
-          if (cls == 1 || cls == 2) flags[((p - ps0) / K) * R + srank[e]] = 1;
+          if (cls == 1 || cls == 2)
+            flags[div_magic((uint32_t)(p - ps0), magic_k) * R + div_magic((uint32_t)e, magic_l)] = 1;
         } else if (e != -1) {
           err = EP_LAYOUT_ERR_INDEX;
         }
@@ -880,21 +890,76 @@ __device__ __forceinline__ void copy_scales(const float* __restrict__ xs, int t,
   }
 }
 
-// Token rows, one wavefront per token, kTokPerBlock per workgroup: MODE 0
-// reads a bf16 row into VGPRs once (NV 16-byte chunks per lane per pass) and
-// stores it to each of the token's K slots; MODE 2 copies pre-quantised e4m3
-// codes and their scales the same way.
-// Workgroups past the tokens do the auxiliary work, after every token block
-// has been issued.
-// Measured against (token, k, piece) workgroups ordered so that the K readers
-// of a piece share an XCD: those win when x is still in the Infinity Cache
-// (85 vs 97 us at the prefill shape) but lose badly from a cold cache (163 vs
-// 112 us), because the K concurrent reads of a piece are not merged into one
-// HBM read; windowed orders that delay the re-reads do not close the gap
-// (118 us at best).  In a real step x arrives cold, so the row is read once.
+// bf16 rows as (token, piece) workgroups of kPieceWaves wavefronts: the piece
+// (kPieceChunks 16-byte chunks, 2 KiB) is read from x once, into LDS, then
+// wavefront w stores it to the slots of pairs w, w + kPieceWaves, ... and tags
+// them on the token's first piece.  Workgroups past the pieces do the
+// auxiliary work, after every piece has been issued.
+// Measured at the prefill shape (per launch warm / cold, and the whole step
+// warm / cold): one wavefront per token holding the row in VGPRs 97 / 112,
+// 199 / 213 us; these workgroups 93 / 104, 195 / 206 us.  The piece size and
+// the workgroup size both matter from a cold cache (1 KiB pieces: 148 us,
+// 2 KiB pieces with 8 wavefronts: 113 us), where the reads of x have to come
+// from HBM while the writes stream out.  The K readers of a piece must stay
+// one read: (token, k, piece) workgroups that each read the piece win while
+// x is in the Infinity Cache (85 us) but lose badly from a cold cache (163
+// us), because the K concurrent reads of a piece are not merged into one HBM
+// read.
+#ifndef EP_PIECE_WAVES
+#define EP_PIECE_WAVES 4
+#endif
+#ifndef EP_PIECE_CHUNKS
+#define EP_PIECE_CHUNKS 128
+#endif
+constexpr int kPieceWaves = EP_PIECE_WAVES;
+constexpr int kPieceThreads = 64 * kPieceWaves;
+constexpr int kPieceChunks = EP_PIECE_CHUNKS;
+static_assert(kPieceChunks % 64 == 0 && kPieceChunks <= kPieceThreads * 4, "piece geometry");
+
+__global__ __launch_bounds__(kPieceThreads) void dispatch_piece_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ slot_of,
+    u32x4* __restrict__ recv_x, int32_t* __restrict__ recv_src, float* __restrict__ recv_w, int N,
+    int K, int R, int P, int64_t item0, int64_t items, int64_t cap, DispatchAux aux) {
+  __shared__ u32x4 piece[kPieceChunks];
+  const int64_t b = item0 + blockIdx.x;
+  if (b >= items) {
+    aux_block<kPieceThreads>(b - items, aux);
+    return;
+  }
+  const int t = (int)(b / P), p = (int)(b % P);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int base = p * kPieceChunks;
+  const int n = min(kPieceChunks, R - base);  // chunks of this piece
+  const u32x4* row = x + (int64_t)t * R + base;
+#pragma unroll
+  for (int j0 = 0; j0 < kPieceChunks; j0 += kPieceThreads) {
+    const int j = j0 + tid;
+    if (j < n) piece[j] = ld16<EP_DISPATCH_NT_LOAD>(row + j);
+  }
+  __syncthreads();
+  for (int k = uniform(tid >> 6); k < K; k += kPieceWaves) {
+    const int s = uniform(slot_of[(int64_t)t * K + k]);
+    if (s < 0 || (int64_t)s >= cap) continue;
+    u32x4* dst = recv_x + (int64_t)s * R + base;
+#pragma unroll
+    for (int i = 0; i < kPieceChunks / 64; i++) {
+      const int c = i * 64 + lane;
+      if (c < n) st16(dst + c, piece[c]);
+    }
+    if (p == 0 && lane == 0) {
+      if (recv_src) recv_src[s] = t;
+      if (recv_w) recv_w[s] = w[(int64_t)t * K + k];
+    }
+  }
+}
+
+// Pre-quantised e4m3 rows, one wavefront per token, kTokPerBlock per
+// workgroup: the codes are read into VGPRs once (NV 16-byte chunks per lane
+// per pass) and stored to each of the token's K slots, with their scales.
+// Workgroups past the tokens do the auxiliary work.
 constexpr int kTokPerBlock = kThreads / 64;
 
-template <int MODE, int NV>  // MODE 0: bf16 rows; 2: pre-quantised e4m3 rows + scales
+template <int NV>
 __global__ __launch_bounds__(kThreads) void dispatch_token_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ xs, const float* __restrict__ w,
     const int32_t* __restrict__ slot_of, u32x4* __restrict__ recv_x,
@@ -909,12 +974,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_token_kernel(
   if (t >= N) return;
   const int lane = threadIdx.x & 63;
   const int myslot = load_slot(slot_of, t, K, lane, cap);
-  if constexpr (MODE == 0) {
-    copy_row<64, NV>(x + (int64_t)t * (H >> 3), recv_x, myslot, K, H >> 3, lane);
-  } else {
-    copy_row<64, NV>(x + (int64_t)t * (H >> 4), recv_x, myslot, K, H >> 4, lane);
-    copy_scales(xs, t, H >> 7, recv_scales, myslot, K, lane);
-  }
+  copy_row<64, NV>(x + (int64_t)t * (H >> 4), recv_x, myslot, K, H >> 4, lane);
+  copy_scales(xs, t, H >> 7, recv_scales, myslot, K, lane);
   write_meta(t, K, lane, myslot, w, recv_src, recv_w);
 }
 
@@ -1470,13 +1531,22 @@ Plan make_plan(const ep_problem_t* p) {
   return pl;
 }
 
-template <int MODE, int NV>
+template <int NV>
 void launch_dispatch_token(int grid, hipStream_t st, const ep_problem_t* p,
                            const ep_dispatch_args_t* a, const DispatchAux& aux) {
-  dispatch_token_kernel<MODE, NV><<<grid, kThreads, 0, st>>>(
+  dispatch_token_kernel<NV><<<grid, kThreads, 0, st>>>(
       (const u32x4*)a->x, a->x_scales, a->topk_weights, a->slot_of, (u32x4*)a->recv_x,
       a->recv_scales, a->recv_src_idx, a->recv_topk_weights, p->num_tokens, p->num_topk,
       p->hidden, a->recv_capacity, aux);
+}
+
+void launch_dispatch_piece(int grid, hipStream_t st, const ep_problem_t* p,
+                           const ep_dispatch_args_t* a, const DispatchAux& aux, int P,
+                           int64_t item0, int64_t items) {
+  dispatch_piece_kernel<<<grid, kPieceThreads, 0, st>>>(
+      (const u32x4*)a->x, a->topk_weights, a->slot_of, (u32x4*)a->recv_x, a->recv_src_idx,
+      a->recv_topk_weights, p->num_tokens, p->num_topk, p->hidden / 8, P, item0, items,
+      a->recv_capacity, aux);
 }
 
 void launch_dispatch_fp8_item(int grid, hipStream_t st, const ep_problem_t* p,
@@ -1526,8 +1596,8 @@ int run_layout(const ep_problem_t* p, const I* topk_idx, int32_t* num_tokens_per
     const size_t mbytes = sizeof(unsigned long long) * (kFusedThreads / 64) * (size_t)E;
     layout_fused_kernel<I><<<pl.B, kFusedThreads, mbytes, st>>>(
         topk_idx, is_token_in_rank, err, num_tokens_per_rank, num_tokens_per_expert,
-        num_recv_per_expert, expert_slot_offset, slot_of, N, K, E, R, L, T, pl.CB, pl.C,
-        p->expert_alignment);
+        num_recv_per_expert, expert_slot_offset, slot_of, N, K, E, R, T, pl.CB, pl.C,
+        p->expert_alignment, magic_of((uint32_t)K), magic_of((uint32_t)L));
     return check_launch("layout_fused");
   }
   layout_count_kernel<I><<<pl.B, kCountThreads, 0, st>>>(
@@ -1754,33 +1824,42 @@ int ep_dispatch_ex(const ep_problem_t* p, const ep_dispatch_args_t* a, void* str
       if ((rc = check_launch("dispatch")) != EP_OK || last) return rc;
     }
   }
-  // row copies: one wavefront per token, then the auxiliary blocks
+  if (mode == 0) {
+    // bf16: (token, 2 KiB piece) workgroups, then the auxiliary blocks
+    const int P = (H / 8 + kPieceChunks - 1) / kPieceChunks;
+    const int64_t items = (int64_t)N * P;
+    const int64_t aux_blocks = (n_aux + kPieceWaves - 1) / kPieceWaves;
+    if (items + aux_blocks == 0) return EP_OK;
+    EP_LOG("dispatch bf16 N=%d H=%d K=%d cap=%lld: piece workgroups=%lld (pieces %d) aux items=%lld "
+           "(tags %lld, zero rows %lld, stats %lld)", N, H, K, (long long)cap, (long long)items, P,
+           (long long)n_aux, (long long)aux.tag_items, (long long)aux.zero_items,
+           (long long)aux.stat_items);
+    for (int64_t item0 = 0;; item0 += kItemLaunch) {
+      const int64_t left = items - item0;
+      const bool last = left <= kItemLaunch;
+      const int64_t grid = last ? left + aux_blocks : kItemLaunch;
+      if (grid > INT32_MAX) return EP_ERR_INVALID_ARG;
+      launch_dispatch_piece((int)grid, st, p, a, aux, P, item0, items);
+      if ((rc = check_launch("dispatch")) != EP_OK || last) return rc;
+    }
+  }
+  // pre-quantised e4m3: one wavefront per token, then the auxiliary blocks
   const int64_t grid = ((int64_t)N + kTokPerBlock - 1) / kTokPerBlock +
                        (n_aux + kTokPerBlock - 1) / kTokPerBlock;
   if (grid > INT32_MAX) return EP_ERR_INVALID_ARG;
   if (grid == 0) return EP_OK;
-  EP_LOG("dispatch %s N=%d H=%d K=%d cap=%lld: token blocks=%d aux items=%lld (tags %lld, "
-         "zero rows %lld, stats %lld)", prequant ? "pre-quantised e4m3" : "bf16", N, H, K,
-         (long long)cap, (N + kTokPerBlock - 1) / kTokPerBlock, (long long)n_aux,
-         (long long)aux.tag_items, (long long)aux.zero_items, (long long)aux.stat_items);
+  EP_LOG("dispatch pre-quantised e4m3 N=%d H=%d K=%d cap=%lld: token blocks=%d aux items=%lld "
+         "(tags %lld, zero rows %lld, stats %lld)", N, H, K, (long long)cap,
+         (N + kTokPerBlock - 1) / kTokPerBlock, (long long)n_aux, (long long)aux.tag_items,
+         (long long)aux.zero_items, (long long)aux.stat_items);
   const int g = (int)grid;
-#define EP_DT(M, NV) launch_dispatch_token<M, NV>(g, st, p, a, aux)
-  if (mode == 0) {
-    if (q <= 1) EP_DT(0, 1);
-    else if (q <= 2) EP_DT(0, 2);
-    else if (q <= 4) EP_DT(0, 4);
-    else if (q <= 7) EP_DT(0, 7);
-    else if (q <= 8) EP_DT(0, 8);
-    else if (q <= 14) EP_DT(0, 14);
-    else EP_DT(0, 16);
-  } else {
-    if (q <= 1) EP_DT(2, 1);
-    else if (q <= 2) EP_DT(2, 2);
-    else if (q <= 4) EP_DT(2, 4);
-    else if (q <= 7) EP_DT(2, 7);
-    else if (q <= 8) EP_DT(2, 8);
-    else EP_DT(2, 16);
-  }
+#define EP_DT(NV) launch_dispatch_token<NV>(g, st, p, a, aux)
+  if (q <= 1) EP_DT(1);
+  else if (q <= 2) EP_DT(2);
+  else if (q <= 4) EP_DT(4);
+  else if (q <= 7) EP_DT(7);
+  else if (q <= 8) EP_DT(8);
+  else EP_DT(16);
 #undef EP_DT
   return check_launch("dispatch");
 }

@@ -99,6 +99,14 @@ def test_ragged_and_multipass_hidden_bf16(H):
     run_case(distinct(np.random.default_rng(H), 96, 4, 32), H=H, E=32, R=4, A=8)
 
 
+@pytest.mark.parametrize("K", [1, 3, 6, 9, 13])
+def test_topk_not_a_multiple_of_the_piece_wavefronts(K):
+    # bf16 rows move as 2 KiB pieces whose slots are shared round robin by the
+    # wavefronts of a workgroup: K above, below and not a multiple of their
+    # number, with a ragged last piece (H = 2088: pieces of 128, 128, 5 chunks)
+    run_case(distinct(np.random.default_rng(K), 80, K, 64), H=2088, E=64, R=4, A=4)
+
+
 @pytest.mark.parametrize("H", [128, 1152, 16384])
 def test_hidden_sizes_fp8(H):
     run_case(distinct(np.random.default_rng(H), 64, 4, 32), H=H, E=32, R=4, A=8, fp8=True)
@@ -128,6 +136,13 @@ def test_k32_many_ranks_and_max_experts():
     rng = np.random.default_rng(6)
     run_case(distinct(rng, 256, 32, 256), H=64, E=256, R=256, A=2)
     run_case(distinct(rng, 512, 8, 1024), H=64, E=1024, R=8, A=32)
+
+
+@pytest.mark.parametrize("N", [4096, 4104])
+def test_layout_paths_at_the_single_launch_threshold(N):
+    # 32768 pairs take the single-launch layout, 32832 the two-launch one
+    rng = np.random.default_rng(N)
+    run_case(rng.integers(-1, 256, size=(N, 8)).astype(np.int32), H=8, E=256, R=8, A=128)
 
 
 def test_ragged_chunks_and_large_n():

@@ -31,7 +31,7 @@ def test_noalloc_layout_matches_layout():
     rng = np.random.default_rng(2024)
     E, R, A, K = 256, 8, 128, 8
     err = torch.full((1,), -1, dtype=torch.int32, device="cuda")
-    for N, bad in ((8192, False), (4096, True), (1024, True)):
+    for N, bad in ((16384, False), (8192, True), (1024, True)):
         say(f"noalloc layout N={N} K={K} E={E} R={R} A={A} bad={bad}")
         idx = torch.from_numpy(_routing(rng, N, K, E, bad)).cuda()
         want = ep.get_layout(idx, E, R, A)
