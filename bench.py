@@ -159,9 +159,10 @@ def ceilings(per_launch_ms, w, slot_of, x, recv_x, eo, nbytes=1 << 30):
     back-to-back launches): linear copy / write / read over 1 GiB with four or
     one 16-byte accesses per thread, and the two traffic patterns of the path
     on the workload's own slot map -- dispatch's (each token row read once and
-    written to its K slots; one wavefront per token, and XCD-placed
-    (token, k, piece) workgroups, which only win while the rows are in the
-    Infinity Cache) and combine's (K slot rows gathered, one row written) --
+    written to its K slots; one wavefront per token, LDS-staged 2 KiB pieces
+    (the dispatch kernel's form), and XCD-placed (token, k, piece)
+    workgroups, which only win while the rows are in the Infinity Cache) and
+    combine's (K slot rows gathered, one row written) --
     with no arithmetic.  GB/s of the patterns use the same algorithmic bytes
     as the kernels they bound."""
     import torch
@@ -172,6 +173,7 @@ def ceilings(per_launch_ms, w, slot_of, x, recv_x, eo, nbytes=1 << 30):
     lib.epc_read_p.argtypes = [vp, i64, ctypes.c_int, vp, vp]
     lib.epc_scatter.argtypes = [vp, vp, vp, i32, i32, i64, vp]
     lib.epc_scatter_items.argtypes = [vp, vp, vp, i32, i32, i64, vp]
+    lib.epc_scatter_pieces.argtypes = [vp, vp, vp, i32, i32, i64, vp]
     lib.epc_gather.argtypes = [vp, vp, vp, i32, i32, i64, vp]
 
     def cur():
@@ -202,6 +204,10 @@ def ceilings(per_launch_ms, w, slot_of, x, recv_x, eo, nbytes=1 << 30):
                                            slot_of.data_ptr(), w.N, w.K, row_b, cur())
         assert fn() == 0
         res["scatter_items_gbs"] = round(disp_b / (per_launch_ms(fn) * 1e-3) / 1e9, 1)
+        fn = lambda: lib.epc_scatter_pieces(x.data_ptr(), recv_x.data_ptr(),  # noqa: E731
+                                            slot_of.data_ptr(), w.N, w.K, row_b, cur())
+        assert fn() == 0
+        res["scatter_pieces_gbs"] = round(disp_b / (per_launch_ms(fn) * 1e-3) / 1e9, 1)
     if w.K <= 8 and row_b <= 16384:
         yt = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
         fn = lambda: lib.epc_gather(eo.data_ptr(), yt.data_ptr(), slot_of.data_ptr(),  # noqa: E731
@@ -272,7 +278,7 @@ def summarize(args):
     f_scale = copy_kib / fetch["copy_kernel"]
     w_scale = copy_kib / write["copy_kernel"]
     disp_b, comb_b = algorithmic_bytes(w)
-    dk = "dispatch_fp8_item_kernel" if w.fp8 else "dispatch_token_kernel"
+    dk = "dispatch_fp8_item_kernel" if w.fp8 else "dispatch_piece_kernel"
     for short, kname, alg in (("dispatch_fp8" if w.fp8 else "dispatch_bf16", dk, disp_b),
                               ("combine", "combine_piece_k_kernel", comb_b)):
         fb = fetch[kname] * f_scale * 1024
@@ -618,8 +624,9 @@ def main():
         result["frac_of_copy_ceiling"] = round(gbs / best_copy, 4)
         frac = {}
         if "scatter_gbs" in c:
-            # the better of the two scatter forms, both timed warm like the kernel
-            best = max(c["scatter_gbs"], c.get("scatter_items_gbs", 0.0))
+            # the best of the scatter forms, all timed warm like the kernel
+            best = max(c["scatter_gbs"], c.get("scatter_items_gbs", 0.0),
+                       c.get("scatter_pieces_gbs", 0.0))
             frac["dispatch"] = round(result["kernel_gbs"]["dispatch"] / best, 4)
         if "gather_gbs" in c:
             frac["combine"] = round(result["kernel_gbs"]["combine"] / c["gather_gbs"], 4)

@@ -11,7 +11,8 @@
 //   scatter             : dispatch's traffic without its arithmetic or tags:
 //                         token row t (R 16-byte chunks) is read once and
 //                         written to the K rows map[t][0..K-1] of dst (one
-//                         wavefront per token, and an XCD-placed item form);
+//                         wavefront per token, LDS-staged 2 KiB pieces, and
+//                         an XCD-placed item form);
 //   gather              : combine's traffic without its arithmetic: the K
 //                         rows map[t][0..K-1] of src are read and one row
 //                         (their XOR, so that no load is dead) is written
@@ -121,6 +122,33 @@ __global__ __launch_bounds__(128) void scatter_items_kernel(const u32x4* __restr
   if (s < 0) return;
   const int c = p * 128 + threadIdx.x;
   if (c < R) __builtin_nontemporal_store(src[(int64_t)t * R + c], dst + (int64_t)s * R + c);
+}
+
+// Scatter as (token, 128-chunk piece) workgroups of four wavefronts: the
+// piece is read once into LDS, then wavefront w stores it to rows
+// map[t][w], map[t][w + 4], ... -- the form of the bf16 dispatch kernel.
+__global__ __launch_bounds__(256) void scatter_pieces_kernel(const u32x4* __restrict__ src,
+                                                             u32x4* __restrict__ dst,
+                                                             const int32_t* __restrict__ map,
+                                                             int N, int K, int R, int P) {
+  __shared__ u32x4 piece[128];
+  const int64_t b = blockIdx.x;
+  const int t = (int)(b / P), p = (int)(b % P);
+  if (t >= N) return;
+  const int base = p * 128, n = min(128, R - base);
+  if ((int)threadIdx.x < n) piece[threadIdx.x] = src[(int64_t)t * R + base + threadIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  for (int k = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); k < K; k += 4) {
+    const int s = __builtin_amdgcn_readfirstlane(map[(int64_t)t * K + k]);
+    if (s < 0) continue;
+    u32x4* d = dst + (int64_t)s * R + base;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int c = i * 64 + lane;
+      if (c < n) __builtin_nontemporal_store(piece[c], d + c);
+    }
+  }
 }
 
 // Gather: one wavefront per (token, piece of 64 chunks); the K slots are
@@ -243,6 +271,22 @@ int epc_scatter(const void* src, void* dst, const int32_t* map, int32_t N, int32
   else if (R <= 64 * 8) scatter_kernel<8><<<blocks, kThreads, 0, st>>>(s, d, map, N, K, R);
   else if (R <= 64 * 14) scatter_kernel<14><<<blocks, kThreads, 0, st>>>(s, d, map, N, K, R);
   else scatter_kernel<16><<<blocks, kThreads, 0, st>>>(s, d, map, N, K, R);
+  return launched();
+}
+
+// The same pattern as LDS-staged (token, piece) workgroups
+// (scatter_pieces_kernel).  Same arguments as epc_scatter.
+int epc_scatter_pieces(const void* src, void* dst, const int32_t* map, int32_t N, int32_t K,
+                       int64_t row_bytes, void* stream) {
+  if (N < 0 || K < 1 || row_bytes <= 0 || row_bytes % 16 || ((uintptr_t)src | (uintptr_t)dst) % 16)
+    return 1;
+  if (N == 0) return 0;
+  const int R = (int)(row_bytes / 16);
+  const int P = (R + 127) / 128;
+  const int64_t blocks = (int64_t)N * P;
+  if (blocks > INT32_MAX) return 1;
+  scatter_pieces_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>(
+      (const u32x4*)src, (u32x4*)dst, map, N, K, R, P);
   return launched();
 }
 
