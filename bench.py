@@ -19,8 +19,10 @@ Prints ONE JSON line.  Extra keys beside the required ones: tokens_per_s,
 hbm_frac, per-kernel times, the roofline of the dominant kernel, the HBM
 ceilings measured on the same box (linear copy / write / read, and dispatch's
 and combine's own access patterns on the workload's slot map) with each
-kernel's fraction of its pattern's ceiling, cold-cache step times, and the CPU
-oracle baseline (threaded and single-threaded).
+kernel's fraction of its pattern's ceiling, cold-cache step times and
+cold-cache times of each call alone (median / p10 / p90, a 1 GiB flush before
+each), the device's clocks, and the CPU oracle baseline (threaded and
+single-threaded).
 """
 import argparse
 import ctypes
@@ -223,7 +225,12 @@ def lds_info():
     a, b = ctypes.c_int64(0), ctypes.c_int64(0)
     if lib.epc_lds_info(ctypes.byref(a), ctypes.byref(b)) != 0:
         return None
-    return {"lds_per_workgroup": a.value, "lds_per_cu": b.value}
+    res = {"lds_per_workgroup": a.value, "lds_per_cu": b.value}
+    c, m, bw = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    if lib.epc_clock_info(ctypes.byref(c), ctypes.byref(m), ctypes.byref(bw)) == 0:
+        res.update({"core_clock_mhz": round(c.value / 1e3), "memory_clock_mhz": round(m.value / 1e3),
+                    "memory_bus_bits": bw.value})
+    return res
 
 
 def _csv_rows(path):
@@ -533,14 +540,38 @@ def main():
             b.record()
         torch.cuda.synchronize()
         us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+        def spread(v):
+            return {"median_us": round(float(np.median(v)), 2),
+                    "p10_us": round(float(np.percentile(v, 10)), 2),
+                    "p90_us": round(float(np.percentile(v, 90)), 2)}
+
+        # each call of the step alone, after its own flush (the inputs of the
+        # later calls are the outputs the steps above left)
+        per_call = {}
+        calls = (("dispatch", do_dispatch), ("combine", do_combine))
+        if not args.ll:
+            calls = (("layout", do_layout),) + calls
+        for name, fn in calls:
+            ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.cold_steps)]
+            for i, (a, b) in enumerate(ce):
+                if args.cold_flush == "read":
+                    flush.sum(dtype=torch.int64)
+                else:
+                    flush.fill_(i)
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            per_call[name] = spread(np.array([a.elapsed_time(b) * 1e3 for a, b in ce]))
         del flush
         disp_b0, comb_b0 = algorithmic_bytes(w)
-        cold = {"median_us": round(float(np.median(us)), 2),
-                "p10_us": round(float(np.percentile(us, 10)), 2),
-                "p90_us": round(float(np.percentile(us, 90)), 2),
-                "gbs_at_median": round((disp_b0 + comb_b0) / (np.median(us) * 1e-6) / 1e9, 1),
-                "steps": args.cold_steps,
-                "flush": f"1 GiB {args.cold_flush} before each step, untimed"}
+        cold = dict(spread(us))
+        cold.update({"gbs_at_median": round((disp_b0 + comb_b0) / (np.median(us) * 1e-6) / 1e9, 1),
+                     "steps": args.cold_steps,
+                     "flush": f"1 GiB {args.cold_flush} before each step or call, untimed",
+                     "per_call": per_call})
 
     lay_ms = 0.0 if args.ll else per_launch_ms(do_layout)
     dis_ms = per_launch_ms(do_dispatch)

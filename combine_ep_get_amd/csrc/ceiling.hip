@@ -241,6 +241,23 @@ int epc_lds_info(int64_t* per_workgroup, int64_t* per_cu) {
   return 0;
 }
 
+// Clocks of the current device as the runtime reports them: peak core clock
+// and memory clock in kHz, memory bus width in bits.  Returns 0, or 3 when an
+// attribute cannot be read.
+int epc_clock_info(int64_t* core_khz, int64_t* mem_khz, int64_t* bus_bits) {
+  int dev = 0, c = 0, m = 0, w = 0;
+  if (!core_khz || !mem_khz || !bus_bits) return 1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&c, hipDeviceAttributeClockRate, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&m, hipDeviceAttributeMemoryClockRate, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&w, hipDeviceAttributeMemoryBusWidth, dev) != hipSuccess)
+    return 3;
+  *core_khz = c;
+  *mem_khz = m;
+  *bus_bits = w;
+  return 0;
+}
+
 // The four-access-per-thread forms (the counter-scaling reference).
 int epc_read(const void* src, int64_t bytes, void* sink, void* stream) {
   return epc_read_p(src, bytes, 4, sink, stream);
