@@ -23,10 +23,12 @@
 //
 // Nothing here is a contraction, so there is no MFMA: every kernel is bound by
 // HBM bandwidth (dispatch, combine) or by latency (layout).  Design points:
-//   - one 64-lane wavefront per token row; 16-byte accesses so that one wave
-//     instruction moves 1 KiB of a row (fully coalesced 128-byte lines);
-//   - the row is read once into VGPRs and stored K times (dispatch), or the K
-//     rows are all put in flight before the fp32 accumulation (combine);
+//   - payload work in small independent items over the pieces of a row:
+//     16-byte accesses, so that one wave instruction moves 1 KiB of a row
+//     (fully coalesced 128-byte lines), and enough items to fill 256 CUs;
+//   - a piece is read once and stored K times (dispatch: through LDS for
+//     bf16, in VGPRs for the fused e4m3 path), or the K rows of a piece are
+//     all put in flight before the fp32 accumulation (combine);
 //   - streaming data uses non-temporal loads/stores so that the 14 KiB rows do
 //     not evict the small metadata from L2 / the Infinity Cache;
 //   - no order-dependent atomics decide a slot: in-block ranks come from
