@@ -1042,10 +1042,7 @@ __global__ __launch_bounds__(kPersistThreads) void dispatch_persist_kernel(
 // of the source's pairs, which gives recv_count, the flags and the running
 // statistics.  Pairs beyond M in a sub-block get no slot and set
 // EP_LAYOUT_ERR_OVERFLOW in the source's flags.
-#ifndef EP_LL_THREADS
-#define EP_LL_THREADS 256
-#endif
-constexpr int kLLThreads = EP_LL_THREADS;
+constexpr int kLLThreads = 256;
 constexpr int kLLWaves = kLLThreads / 64;
 
 // MODE 0: bf16 rows; 1: fused e4m3 quantisation; 2: pre-quantised e4m3 codes
