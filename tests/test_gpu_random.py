@@ -16,7 +16,9 @@ from .gpu_util import check_combine, check_layout, dev_bf16, host_u16, host_u8, 
 pytestmark = pytest.mark.gpu
 
 
-def _case(seed):
+def _case(seed, wide=False):
+    """wide: rows of up to 3,192 bf16 channels or 24 e4m3 groups (several
+    dispatch pieces with a ragged last one), for seeds of their own."""
     rng = np.random.default_rng(7000 + seed)
     R = int(rng.choice([1, 2, 3, 4, 8]))
     E = R * int(rng.integers(1, 9))
@@ -24,7 +26,10 @@ def _case(seed):
     N = R * int(rng.integers(0, 40))
     A = int(rng.choice([1, 1, 2, 3, 8, 16]))
     fp8 = bool(rng.random() < 0.4)
-    H = 128 * int(rng.integers(1, 5)) if fp8 else 8 * int(rng.integers(1, 80))
+    if wide:
+        H = 128 * int(rng.integers(1, 25)) if fp8 else 8 * int(rng.integers(1, 400))
+    else:
+        H = 128 * int(rng.integers(1, 5)) if fp8 else 8 * int(rng.integers(1, 80))
     idx = rng.integers(-1, E, size=(N, K)).astype(np.int32)
     w = rng.standard_normal((N, K)).astype(np.float32)
     x = (rng.standard_normal((N, H)).astype(np.float32) * rng.uniform(0.01, 100))
@@ -36,7 +41,17 @@ def _case(seed):
 
 @pytest.mark.parametrize("seed", range(40))
 def test_random_shape_parity(seed):
-    c = _case(seed)
+    _run(seed, _case(seed))
+
+
+@pytest.mark.parametrize("seed", range(100, 112))
+def test_random_shape_parity_wide_rows(seed):
+    c = _case(seed, wide=True)
+    c["budget"] = 0      # the ordinary launches: rows in several pieces
+    _run(seed, c)
+
+
+def _run(seed, c):
     N, H, K, E, R, A, fp8 = c["N"], c["H"], c["K"], c["E"], c["R"], c["A"], c["fp8"]
     say(f"random seed={seed}: N={N} H={H} K={K} E={E} R={R} A={A} fp8={fp8} "
         f"budget={c['budget']}")
