@@ -52,15 +52,13 @@
 
 // Cache policy of the streaming accesses (measured on MI355X): token rows
 // read by dispatch use ordinary loads, expert rows read by combine use
-// non-temporal loads, and all payload stores are non-temporal.
+// non-temporal loads; dispatch stores its rows non-temporally, combine writes
+// y through to memory (st16p below).
 #ifndef EP_DISPATCH_NT_LOAD
 #define EP_DISPATCH_NT_LOAD 0
 #endif
 #ifndef EP_COMBINE_NT_LOAD
 #define EP_COMBINE_NT_LOAD 1
-#endif
-#ifndef EP_NT_STORE
-#define EP_NT_STORE 1
 #endif
 
 namespace {
@@ -79,12 +77,40 @@ __device__ __forceinline__ u32x4 ld16(const u32x4* p) {
   else return *p;
 }
 
-__device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
-#if EP_NT_STORE
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
+// Payload stores of dispatch: non-temporal (EP_DISPATCH_STORE 0) or ordinary (1).
+template <int POL>
+__device__ __forceinline__ void st16p(u32x4* p, u32x4 v) {
+  if constexpr (POL == 0) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+#ifndef EP_DISPATCH_STORE
+#define EP_DISPATCH_STORE 0
 #endif
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) { st16p<EP_DISPATCH_STORE>(p, v); }
+
+// Stores of combine's output y: chunk c of a token's row.  EP_COMBINE_STORE 2
+// writes it through to memory (device scope) with a buffer store over the row
+// (whose base is uniform per wavefront); 0 / 1 as st16p.
+// Measured per prefill step (layout + dispatch + combine) with y written
+// through instead of non-temporally: 197 -> 193 us back to back and 206 ->
+// 201 us after a read pass over 1 GiB, because no dirty lines of y are left
+// for the next kernel to write back; 4 us slower after a write pass (dirty
+// lines of other data in the caches).  Writing the dispatched rows through as
+// well gains another 2 us back to back but loses 3-5 us from a cold cache, so
+// dispatch stays non-temporal.
+#ifndef EP_COMBINE_STORE
+#define EP_COMBINE_STORE 2
+#endif
+constexpr int kCpolDeviceScope = 16;  // SC1 in the cache-policy operand of gfx950 buffer ops
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+__device__ __forceinline__ void st16y(u32x4* row, int H8, int c, u32x4 v) {
+  if constexpr (EP_COMBINE_STORE == 2) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(row, 0, H8 * 16, kBufferWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, c * 16, 0, kCpolDeviceScope);
+  } else {
+    st16p<EP_COMBINE_STORE>(row + c, v);
+  }
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -1238,7 +1264,7 @@ __device__ __forceinline__ void combine_store(const float (&acc)[NV][8], u32x4* 
       u32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; q++) o[q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
-      st16(yrow + c, o);
+      st16y(yrow, H8, c, o);
     }
   }
 }
@@ -1308,7 +1334,7 @@ __global__ __launch_bounds__(64) void combine_piece_k_kernel(
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; q++) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-    st16(y + (int64_t)t * H8 + c, o);
+    st16y(y + (int64_t)t * H8, H8, c, o);
   }
 }
 
