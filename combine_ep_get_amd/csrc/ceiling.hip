@@ -16,7 +16,7 @@
 //   gather              : combine's traffic without its arithmetic: the K
 //                         rows map[t][0..K-1] of src are read and one row
 //                         (their XOR, so that no load is dead) is written
-//                         to dst[t].
+//                         to dst[t], through to memory as combine writes y.
 // The map is the real slot map of a workload (slot_of), so the addresses are
 // exactly the EP kernels'.  Rows named -1 are skipped (scatter) or read as
 // row 0 (gather, like combine's branch-free loads).
@@ -174,7 +174,13 @@ __global__ __launch_bounds__(64) void gather_kernel(const u32x4* __restrict__ sr
   u32x4 x = v[0];
 #pragma unroll
   for (int k = 1; k < K; k++) x ^= v[k];
-  if (c < R) __builtin_nontemporal_store(x, dst + (int64_t)t * R + c);
+  // written through to memory over the token's row, like the combine kernel
+  // (a buffer store with the device-scope cache bit)
+  if (c < R) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(dst + (int64_t)t * R, 0, R * 16, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, c * 16, 0, 16);
+  }
 }
 
 int64_t blocks_of(int64_t n16, int per) { return (n16 + (int64_t)kThreads * per - 1) / ((int64_t)kThreads * per); }

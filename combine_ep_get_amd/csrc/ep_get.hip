@@ -53,7 +53,7 @@
 // Cache policy of the streaming accesses (measured on MI355X): token rows
 // read by dispatch use ordinary loads, expert rows read by combine use
 // non-temporal loads; dispatch stores its rows non-temporally, combine writes
-// y through to memory (st16p below).
+// y through to memory (st16y below).
 #ifndef EP_DISPATCH_NT_LOAD
 #define EP_DISPATCH_NT_LOAD 0
 #endif
