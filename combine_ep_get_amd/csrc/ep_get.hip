@@ -1528,7 +1528,7 @@ int validate_payload(const ep_problem_t* p) {
   int rc = validate_layout(p);
   if (rc != EP_OK) return rc;
   const int H = p->hidden;
-  if (H <= 0 || H % 8 != 0) return EP_ERR_INVALID_ARG;
+  if (H <= 0 || H > EP_MAX_HIDDEN || H % 8 != 0) return EP_ERR_INVALID_ARG;
   if (p->use_fp8 != 0 && p->use_fp8 != 1) return EP_ERR_INVALID_ARG;
   if (p->use_fp8 && H % 128 != 0) return EP_ERR_INVALID_ARG;
   return EP_OK;

@@ -67,6 +67,7 @@ enum {
 #define EP_MAX_EXPERTS 1024
 #define EP_MAX_RANKS 256
 #define EP_MAX_TOPK 32
+#define EP_MAX_HIDDEN (1 << 24)
 
 /* Bits of the device error word read by ep_layout_error, and of the
  * per-source flags of ep_ll_dispatch. */
@@ -75,7 +76,8 @@ enum {
 
 /* Problem descriptor (host memory, read during the call only).
  *   num_tokens        N >= 0, all virtual source ranks together, N % R == 0
- *   hidden            H > 0, H % 8 == 0; H % 128 == 0 when use_fp8
+ *   hidden            H, 1..EP_MAX_HIDDEN, H % 8 == 0; H % 128 == 0 when
+ *                     use_fp8 (the kernels index a row's bytes in 32 bits)
  *   num_topk          K, 1..EP_MAX_TOPK
  *   num_experts       E, 1..EP_MAX_EXPERTS, E % R == 0 (the experts divide
  *                     evenly over the ranks, as DeepEP asserts)

@@ -118,7 +118,8 @@ def test_noalloc_layout_missing_outputs_and_scratch_bound():
 def test_payload_rejects_bad_descriptors():
     L = ep.lib()
     fake = ctypes.c_void_p(256)
-    for kw in (dict(hidden=0), dict(hidden=12), dict(hidden=200, use_fp8=True)):
+    for kw in (dict(hidden=0), dict(hidden=12), dict(hidden=200, use_fp8=True),
+               dict(hidden=(1 << 24) + 8), dict(hidden=(1 << 24) + 128, use_fp8=True)):
         p = _p(**kw)
         assert L.ep_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
                              fake, 10 ** 6, None) == 1
