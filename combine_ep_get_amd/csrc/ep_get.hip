@@ -30,7 +30,9 @@
 //     bf16, in VGPRs for the fused e4m3 path), or the K rows of a piece are
 //     all put in flight before the fp32 accumulation (combine);
 //   - streaming data uses non-temporal loads/stores so that the 14 KiB rows do
-//     not evict the small metadata from L2 / the Infinity Cache;
+//     not evict the small metadata from L2 / the Infinity Cache, except that
+//     combine writes y through to memory, leaving no dirty lines of it for
+//     the next kernel to write back;
 //   - no order-dependent atomics decide a slot: in-block ranks come from
 //     per-wavefront 64-bit LDS masks (atomic OR, commutative) plus popcount,
 //     so every output is deterministic run to run;
