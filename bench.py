@@ -21,8 +21,8 @@ ceilings measured on the same box (linear copy / write / read, and dispatch's
 and combine's own access patterns on the workload's slot map) with each
 kernel's fraction of its pattern's ceiling, cold-cache step times and
 cold-cache times of each call alone (median / p10 / p90, a 1 GiB flush before
-each), the device's clocks, and the CPU oracle baseline (threaded and
-single-threaded).
+each), the same step times after a 1 GiB write pass (dirty caches), the
+device's clocks, and the CPU oracle baseline (threaded and single-threaded).
 """
 import argparse
 import ctypes
@@ -565,13 +565,29 @@ def main():
                 b.record()
             torch.cuda.synchronize()
             per_call[name] = spread(np.array([a.elapsed_time(b) * 1e3 for a, b in ce]))
+        # whole steps after the other kind of pass too: a write pass leaves
+        # dirty lines of other data in the caches, which the step then pays for
+        other = "write" if args.cold_flush == "read" else "read"
+        oe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.cold_steps)]
+        for i, (a, b) in enumerate(oe):
+            if other == "read":
+                flush.sum(dtype=torch.int64)
+            else:
+                flush.fill_(i)
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        other_us = np.array([a.elapsed_time(b) * 1e3 for a, b in oe])
         del flush
         disp_b0, comb_b0 = algorithmic_bytes(w)
         cold = dict(spread(us))
         cold.update({"gbs_at_median": round((disp_b0 + comb_b0) / (np.median(us) * 1e-6) / 1e9, 1),
                      "steps": args.cold_steps,
                      "flush": f"1 GiB {args.cold_flush} before each step or call, untimed",
-                     "per_call": per_call})
+                     "per_call": per_call,
+                     f"after_{other}_flush": spread(other_us)})
 
     lay_ms = 0.0 if args.ll else per_launch_ms(do_layout)
     dis_ms = per_launch_ms(do_dispatch)
